@@ -1,0 +1,152 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV-cache attention for AMD MI355X (gfx950).
+ *
+ * The operations are those of a paged KV cache as the mini-vLLM pages describe
+ * it:
+ *   - K/V storage is split into fixed-size blocks of tokens, 16 per block
+ *     (page "轻量级的vLLM", mini-vllm write-up, section 核心机制一：分页 KV Cache);
+ *   - each sequence owns a block table mapping its logical blocks to physical
+ *     ones, and attention finds the real K and V through it (page
+ *     "从零实现一个 mini vLLM--开篇", section "5. 这个系列会怎么展开", stages four
+ *     and five; page "vllm-v0 版本介绍", section 为什么需要推理框架？);
+ *   - decode computes only the new token's K/V, appends them to the cache, and
+ *     the new token attends to every cached token of its sequence (page
+ *     "从零实现一个 mini vLLM--开篇", section "2. LLM 推理到底在慢什么");
+ *   - chunked prefill is named as a later topic (same page, section 5, stage
+ *     six); its reading here is stated at pa_prefill_chunk.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Memory     All array arguments are DEVICE pointers (hipMalloc'd or torch
+ *             CUDA/HIP tensors), row-major and contiguous.  The caller owns
+ *             every buffer, the workspace included; the library never allocates
+ *             or frees device memory and keeps no state between calls.
+ *  Layouts    q / key / value / out     [rows, heads, head_dim]
+ *             k_cache / v_cache         [num_blocks, block_size, num_kv_heads, head_dim]
+ *             block_tables              [num_seqs, max_blocks_per_seq] int32
+ *             context_lens              [num_seqs] int32
+ *             slot_mapping              [num_tokens] int32
+ *  Heads      Query head h reads kv head h / (num_q_heads / num_kv_heads):
+ *             consecutive query heads share one kv head (grouped-query heads).
+ *  Types      dtype applies to q, key, value, caches and out alike.  Attention
+ *             accumulates in fp32; out is rounded to nearest even.
+ *  Streams    stream is a hipStream_t (NULL = the legacy default stream).  Every
+ *             call only enqueues work on it and returns; results are ready when
+ *             the stream reaches that point.  Work on one stream runs in call
+ *             order, so enqueue pa_reshape_and_cache before the attention call
+ *             that must see the appended tokens.
+ *  Errors     Every entry point returns a pa_status.  Argument checks run on the
+ *             host before anything is enqueued; on an error nothing is launched
+ *             and no buffer is touched.  The library never aborts or throws.
+ *             Values inside device arrays are NOT checked (that would need a
+ *             device-to-host copy): block ids must lie in [0, num_blocks),
+ *             context_lens[s] <= max_blocks_per_seq * block_size, slots in one
+ *             pa_reshape_and_cache call must be distinct, and every table entry
+ *             below ceil(context_lens[s] / block_size) must be valid.  Table
+ *             entries past that point are never read.
+ *  Supported  block_size 16; head_dim 64 or 128; num_q_heads a multiple of
+ *             num_kv_heads with at most 64 query heads per kv head; dtypes
+ *             PA_F32 and PA_BF16 (pa_prefill_chunk: PA_BF16 only).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_F32 = 0,  /* IEEE binary32 */
+    PA_BF16 = 1  /* bfloat16 */
+} pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_EINVAL = -1,       /* an argument is out of its documented range */
+    PA_EUNSUPPORTED = -2, /* valid, but a shape or dtype this build does not handle */
+    PA_EWORKSPACE = -3,   /* workspace pointer NULL or smaller than required */
+    PA_ELAUNCH = -4       /* the HIP runtime refused a launch */
+} pa_status;
+
+/*
+ * KV append.  For every new token i in [0, num_tokens) with
+ * slot = slot_mapping[i] >= 0, copy key[i] ([num_kv_heads, head_dim]) into
+ * k_cache[slot / block_size, slot % block_size] and value[i] into v_cache at
+ * the same place, bit for bit.  Negative slots (padding tokens) are skipped.
+ * key, value: [num_tokens, num_kv_heads, head_dim].  Slots must be distinct
+ * and below num_blocks * block_size.  num_tokens == 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void *key, const void *value,
+                         void *k_cache, void *v_cache,
+                         const int32_t *slot_mapping, int32_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, pa_dtype dtype, void *stream);
+
+/*
+ * Bytes of workspace pa_decode needs for these shapes (0 if none).  The result
+ * is an upper bound that holds for every context length the block table
+ * allows; a workspace of this size can be reused by any later call with the
+ * same or smaller shapes.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * Paged-attention decode: one query row per sequence.  For sequence s and
+ * query head h, with n = context_lens[s] (the cached tokens of s, the token
+ * being decoded included) and kv = h / (num_q_heads / num_kv_heads):
+ *   x_t = scale * <q[s,h,:], K_t>,  t = 0..n-1,
+ *   out[s,h,:] = sum_t softmax(x)_t * V_t,
+ * where token t of s lives in physical block block_tables[s, t / block_size]
+ * at offset t % block_size.  n == 0 writes zeros.
+ * q, out: [num_seqs, num_q_heads, head_dim].  workspace: device memory of at
+ * least pa_decode_workspace_size(...) bytes (may be NULL when that is 0); it
+ * holds split-context partial results between the kernels of one call, so
+ * calls that overlap in time must not share it.
+ */
+int pa_decode(void *out, const void *q,
+              const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, int32_t max_blocks_per_seq,
+              const int32_t *context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace pa_prefill_chunk needs (currently always 0). */
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows,
+                                 int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * Chunked prefill.  Sequence s owns query rows query_start_loc[s] ..
+ * query_start_loc[s+1]-1: its c = query_start_loc[s+1] - query_start_loc[s]
+ * newest tokens, whose K/V must already be in the cache (append them with
+ * pa_reshape_and_cache first).  Row i of the chunk sits at absolute position
+ * p = context_lens[s] - c + i and attends causally to tokens 0..p inclusive of
+ * its own sequence, through the block table, with the same formula as
+ * pa_decode.  0 <= c <= context_lens[s] is required.
+ * q, out: [query_start_loc[num_seqs], num_q_heads, head_dim]; query_start_loc:
+ * [num_seqs + 1] int32, non-decreasing, starting at 0.  total_query_rows is
+ * query_start_loc[num_seqs] (the host's copy).
+ */
+int pa_prefill_chunk(void *out, const void *q,
+                     const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *query_start_loc, int32_t total_query_rows,
+                     const int32_t *context_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable text for a pa_status value. */
+const char *pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,178 @@
+// pa_api.hip -- the C ABI of libpa.so (declared in include/pa.h).
+//
+// Host code only: argument checks (all before anything is enqueued), workspace
+// layout, grid sizing and dispatch to the kernel instances.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kMaxGroup = 64;  // query heads per kv head handled (8 groups of 8)
+
+int check_dtype(pa_dtype dtype) {
+    return (dtype == PA_F32 || dtype == PA_BF16) ? PA_OK : PA_EUNSUPPORTED;
+}
+
+int elem_bytes(pa_dtype dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+int check_cache_shape(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks) {
+    if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0) return PA_EINVAL;
+    if (num_blocks > INT32_MAX / block_size) return PA_EINVAL;  // slots must fit int32
+    if (block_size != 16) return PA_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_EUNSUPPORTED;
+    return PA_OK;
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return PA_EINVAL;
+    if (num_q_heads / num_kv_heads > kMaxGroup) return PA_EUNSUPPORTED;
+    return PA_OK;
+}
+
+// Query heads handled by one wave (a power of two, at most 8).
+int heads_per_wave(int group) {
+    int gp = 1;
+    while (gp < group && gp < 8) gp *= 2;
+    return gp;
+}
+
+int decode_max_parts(int32_t max_blocks_per_seq) {
+    const long long tokens = (long long)max_blocks_per_seq * 16;
+    return (int)((tokens + pa::kDecodePartTokens - 1) / pa::kDecodePartTokens);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_ws_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
+    const int parts = decode_max_parts(max_blocks_per_seq);
+    if (parts <= 1) return 0;
+    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
+    return align256(rows * 2 * sizeof(float)) + align256(rows * head_dim * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK: success";
+        case PA_EINVAL: return "PA_EINVAL: an argument is out of its documented range";
+        case PA_EUNSUPPORTED: return "PA_EUNSUPPORTED: shape or dtype not supported by this build";
+        case PA_EWORKSPACE: return "PA_EWORKSPACE: workspace missing or too small";
+        case PA_ELAUNCH: return "PA_ELAUNCH: the HIP runtime refused a kernel launch";
+        default: return "unknown pa_status";
+    }
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                         void* stream) {
+    int rc = check_dtype(dtype);
+    if (rc) return rc;
+    if (num_tokens < 0) return PA_EINVAL;
+    rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
+    if (rc) return rc;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_EINVAL;
+    const long long row_bytes = (long long)num_kv_heads * head_dim * elem_bytes(dtype);
+    if (row_bytes > INT32_MAX) return PA_EUNSUPPORTED;
+    hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                                (int)row_bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size) {
+    (void)num_kv_heads;
+    (void)block_size;
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0) return 0;
+    return decode_ws_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq);
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    int rc = check_dtype(dtype);
+    if (rc) return rc;
+    if (num_seqs < 0) return PA_EINVAL;
+    rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
+    if (rc) return rc;
+    rc = check_heads(num_q_heads, num_kv_heads);
+    if (rc) return rc;
+    if (max_blocks_per_seq <= 0 || max_blocks_per_seq > INT32_MAX / block_size) return PA_EINVAL;
+    if (!isfinite(scale)) return PA_EINVAL;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+    const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_EWORKSPACE;
+
+    const int group = num_q_heads / num_kv_heads;
+    const int gp = heads_per_wave(group);
+    pa::DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.groups_per_kv = (group + gp - 1) / gp;
+    a.max_parts = decode_max_parts(max_blocks_per_seq);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const long long grid = (long long)a.max_parts * num_seqs * num_kv_heads * a.groups_per_kv;
+    if (grid > INT32_MAX) return PA_EUNSUPPORTED;
+    if (need > 0) {
+        const size_t rows = (size_t)num_seqs * num_q_heads * a.max_parts;
+        a.ws_ml = static_cast<float*>(workspace);
+        a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * 2 * sizeof(float)));
+    } else {
+        a.ws_ml = nullptr;
+        a.ws_acc = nullptr;
+    }
+    hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size) {
+    (void)num_seqs; (void)total_query_rows; (void)num_q_heads;
+    (void)head_dim; (void)max_blocks_per_seq; (void)block_size;
+    return 0;
+}
+
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* query_start_loc, int32_t total_query_rows,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                     float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    (void)workspace; (void)workspace_bytes; (void)stream;
+    int rc = check_dtype(dtype);
+    if (rc) return rc;
+    if (num_seqs < 0 || total_query_rows < 0) return PA_EINVAL;
+    rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
+    if (rc) return rc;
+    rc = check_heads(num_q_heads, num_kv_heads);
+    if (rc) return rc;
+    if (max_blocks_per_seq <= 0 || max_blocks_per_seq > INT32_MAX / block_size) return PA_EINVAL;
+    if (!isfinite(scale)) return PA_EINVAL;
+    if (num_seqs == 0 || total_query_rows == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
+        return PA_EINVAL;
+    return PA_EUNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// pa_cache.hip -- KV append: copy each new token's K and V rows into the cache
+// slot named by the slot mapping (decode appends only the new token's key and
+// value: page "从零实现一个 mini vLLM--开篇", section "2. LLM 推理到底在慢什么";
+// blocks of 16 tokens: page "轻量级的vLLM", section 核心机制一：分页 KV Cache).
+//
+// One token's row ([num_kv_heads, head_dim]) is contiguous both in the input
+// and in the cache (at slot * row_bytes), so the append is a gather-free row
+// copy: every thread moves one 16-byte vector of K or V.  The copy is bit
+// exact for any element type.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int num_tokens,
+    int row_vecs) {
+    const long long per_tensor = (long long)num_tokens * row_vecs;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * per_tensor;
+         i += (long long)gridDim.x * blockDim.x) {
+        const bool is_v = i >= per_tensor;
+        const long long j = is_v ? i - per_tensor : i;
+        const int tok = (int)(j / row_vecs);
+        const int vec = (int)(j % row_vecs);
+        const int slot = slot_mapping[tok];
+        if (slot < 0) continue;
+        const uint4* src = is_v ? value : key;
+        uint4* dst = is_v ? v_cache : k_cache;
+        dst[(long long)slot * row_vecs + vec] = src[j];
+    }
+}
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int num_tokens, int row_bytes,
+                                    hipStream_t stream) {
+    const int row_vecs = row_bytes / 16;
+    const long long total = 2LL * num_tokens * row_vecs;
+    long long blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), slot_mapping,
+                       num_tokens, row_vecs);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,85 @@
+// pa_device.h -- device-side helpers shared by the libpa kernels (gfx950 only).
+//
+// Wave64 lane exchanges use DPP row patterns and the gfx950 permlane swaps;
+// bf16 arithmetic uses v_dot2_f32_bf16 (two bf16 products accumulated into an
+// fp32) and v_cvt_pk_bf16_f32 (round to nearest even).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockTokens = 16;  // tokens per KV block
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// DPP controls (row = 16 lanes).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppRowRor8 = 0x128;     // lane i <- lane (i+8) mod 16 within a row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 lanes that share lane bits 3..5 (an aligned group of 8).
+__device__ __forceinline__ float sum_lanes8(float x) {
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppHalfMirror>(x);
+    return x;
+}
+
+// Reduce across lane bits 3..5 (the eight groups of 8 lanes): xor 8 within a
+// row by DPP, xor 16 and xor 32 by the gfx950 permlane swaps.
+__device__ __forceinline__ float max_groups8(float x) {
+    x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+    {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return x;
+}
+
+__device__ __forceinline__ float sum_groups8(float x) {
+    x += dpp_f32<kDppRowRor8>(x);
+    {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two fp32 values to a packed bf16 pair (lo in bits 0..15), nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,197 @@
+"""Thin ctypes binding over libpa.so (C ABI in include/pa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libpa.so.  Tensors are torch CUDA/HIP tensors on the current
+device; their data pointers and the current stream are handed to the library
+as they are.  The library must have been built (``python -m
+paged_kv_cache_275_amd.build``); if it is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpa.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "pa.h")
+
+PA_F32 = 0
+PA_BF16 = 1
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH = 0, -1, -2, -3, -4
+BLOCK_SIZE = 16
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {text} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpa.so and declare its signatures; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_275_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.pa_reshape_and_cache.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i64, ctypes.c_int, p]
+    lib.pa_reshape_and_cache.restype = ctypes.c_int
+    lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_workspace_size.restype = sz
+    lib.pa_decode.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
+                              ctypes.c_int, p, sz, p]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_prefill_workspace_size.restype = sz
+    lib.pa_prefill_chunk.argtypes = [p, p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32, i64,
+                                     f32, ctypes.c_int, p, sz, p]
+    lib.pa_prefill_chunk.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER) -> list:
+    """Names of the functions include/pa.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(lib, fn: str, rc: int) -> None:
+    if rc != PA_OK:
+        raise PAError(fn, rc, lib.pa_status_string(rc).decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported element type {t.dtype}; use float32 or bfloat16")
+
+
+def _need(t, name: str, dtype=None, dim: Optional[int] = None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+
+
+def _stream_handle(t, stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return s.cuda_stream
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """k_cache[slot // 16, slot % 16] = key[i] (and value), for slot_mapping[i] >= 0."""
+    import torch
+    lib = load_library()
+    _need(key, "key", dim=3)
+    _need(value, "value", key.dtype, 3)
+    _need(k_cache, "k_cache", key.dtype, 4)
+    _need(v_cache, "v_cache", key.dtype, 4)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    nb, bs, hkv, d = k_cache.shape
+    if tuple(key.shape[1:]) != (hkv, d) or value.shape != key.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("key/value [T, Hkv, D] must match caches [NB, 16, Hkv, D]")
+    if slot_mapping.shape[0] != key.shape[0]:
+        raise ValueError("slot_mapping must have one entry per token")
+    rc = lib.pa_reshape_and_cache(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
+                                  v_cache.data_ptr(), slot_mapping.data_ptr(), key.shape[0], hkv,
+                                  d, bs, nb, _dtype_code(key), _stream_handle(key, stream))
+    _check(lib, "pa_reshape_and_cache", rc)
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          block_size=BLOCK_SIZE) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                       head_dim, max_blocks_per_seq, block_size))
+
+
+def decode_workspace(q, k_cache, block_tables):
+    """Allocate (torch, uint8) a workspace big enough for decode() with these shapes."""
+    import torch
+    n = decode_workspace_size(q.shape[0], q.shape[1], k_cache.shape[2], q.shape[2],
+                              block_tables.shape[1], k_cache.shape[1])
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace=None,
+           stream=None) -> None:
+    """Paged-attention decode into out [S, Hq, D]."""
+    import torch
+    lib = load_library()
+    _need(q, "q", dim=3)
+    _need(out, "out", q.dtype, 3)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    s, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    if out.shape != q.shape or dk != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q/out and the caches")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    if workspace is None:
+        workspace = decode_workspace(q, k_cache, block_tables)
+    rc = lib.pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                       block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), s,
+                       hq, hkv, d, bs, nb, float(scale), _dtype_code(q), workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), _stream_handle(q, stream))
+    _check(lib, "pa_decode", rc)
+
+
+def prefill_workspace_size(num_seqs, total_query_rows, num_q_heads, head_dim, max_blocks_per_seq,
+                           block_size=BLOCK_SIZE) -> int:
+    return int(load_library().pa_prefill_workspace_size(num_seqs, total_query_rows, num_q_heads,
+                                                        head_dim, max_blocks_per_seq, block_size))
+
+
+def prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                  scale: float, workspace=None, stream=None) -> None:
+    """Causal chunked prefill into out [rows, Hq, D] (see pa_prefill_chunk)."""
+    import torch
+    lib = load_library()
+    _need(q, "q", dim=3)
+    _need(out, "out", q.dtype, 3)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    rows, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    sp = context_lens.shape[0]
+    if out.shape != q.shape or dk != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q/out and the caches")
+    if block_tables.shape[0] != sp or query_start_loc.shape[0] != sp + 1:
+        raise ValueError("block_tables [S, MB] and query_start_loc [S+1] must match context_lens [S]")
+    need = prefill_workspace_size(sp, rows, hq, d, block_tables.shape[1], bs)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.pa_prefill_chunk(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                              block_tables.data_ptr(), block_tables.shape[1],
+                              query_start_loc.data_ptr(), rows, context_lens.data_ptr(), sp, hq,
+                              hkv, d, bs, nb, float(scale), _dtype_code(q), ws_ptr, ws_bytes,
+                              _stream_handle(q, stream))
+    _check(lib, "pa_prefill_chunk", rc)

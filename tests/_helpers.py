@@ -80,3 +80,29 @@ def bf16_bits_from_float(x: np.ndarray) -> np.ndarray:
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- tolerances
+F32_ATOL = 1e-5          # fp32 attention: max-abs
+BF16_ATOL = 2e-2         # bf16 attention: max-abs ...
+BF16_ROW_RTOL = 1e-2     # ... and per (row, head): max|gpu - ref| / max|ref|
+
+
+def attention_errors(got: np.ndarray, ref: np.ndarray):
+    """(max-abs error, worst per-(row, head) relative error) of [R, H, D] arrays."""
+    diff = np.abs(got - ref)
+    scale = np.abs(ref).max(axis=-1)
+    row = diff.max(axis=-1) / np.where(scale > 0, scale, 1.0)
+    return float(diff.max()) if diff.size else 0.0, float(row.max()) if row.size else 0.0
+
+
+def assert_attention_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mx, rel = attention_errors(got, ref)
+    if dtype == "f32":
+        assert mx <= F32_ATOL, f"{what}: fp32 max-abs error {mx:.3e} > {F32_ATOL}"
+    else:
+        assert mx <= BF16_ATOL, f"{what}: bf16 max-abs error {mx:.3e} > {BF16_ATOL}"
+        assert rel <= BF16_ROW_RTOL, f"{what}: bf16 row-relative error {rel:.3e} > {BF16_ROW_RTOL}"
+    return mx, rel

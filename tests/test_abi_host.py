@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/pa.h declares, and rejects bad arguments on the host before any HIP
+call (fake non-null pointers are never dereferenced on these paths)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from paged_kv_cache_275_amd import ops
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from paged_kv_cache_275_amd import build
+        build.build()
+    return ops.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = ops.header_functions()
+    assert {"pa_reshape_and_cache", "pa_decode", "pa_prefill_chunk", "pa_decode_workspace_size",
+            "pa_prefill_workspace_size", "pa_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libpa.so does not export {n}"
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.pa_status_string(code).startswith(b"PA_")
+    assert lib.pa_status_string(123) == b"unknown pa_status"
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=4, cl=FAKE, s=2, hq=8, hkv=2, d=128,
+             bs=16, nb=64, scale=0.1, dtype=ops.PA_BF16, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["s"],
+                         a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+                         a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), ops.PA_EINVAL),               # heads not a multiple
+    (dict(hkv=0), ops.PA_EINVAL),
+    (dict(d=96), ops.PA_EUNSUPPORTED),
+    (dict(bs=32), ops.PA_EUNSUPPORTED),
+    (dict(dtype=7), ops.PA_EUNSUPPORTED),
+    (dict(hq=130, hkv=2), ops.PA_EUNSUPPORTED),        # 65 query heads per kv head
+    (dict(s=-1), ops.PA_EINVAL),
+    (dict(nb=0), ops.PA_EINVAL),
+    (dict(nb=(1 << 31) // 16 + 1), ops.PA_EINVAL),     # slots overflow int32
+    (dict(mb=0), ops.PA_EINVAL),
+    (dict(scale=float("nan")), ops.PA_EINVAL),
+    (dict(q=None), ops.PA_EINVAL),
+    (dict(bt=None), ops.PA_EINVAL),
+    (dict(mb=4096, ws=None), ops.PA_EWORKSPACE),
+    (dict(mb=4096, ws_bytes=16), ops.PA_EWORKSPACE),
+])
+def test_decode_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _decode(lib, s=0, q=None, out=None) == ops.PA_OK
+
+
+def test_decode_workspace_size(lib):
+    # short tables fit one partition: no workspace
+    assert lib.pa_decode_workspace_size(128, 32, 8, 128, 4, 16) == 0
+    big = lib.pa_decode_workspace_size(16, 16, 8, 128, 4096, 16)
+    assert big > 0
+    # monotone in every shape argument
+    assert lib.pa_decode_workspace_size(32, 16, 8, 128, 4096, 16) >= big
+    assert lib.pa_decode_workspace_size(16, 32, 8, 128, 4096, 16) >= big
+    assert lib.pa_decode_workspace_size(16, 16, 8, 128, 8192, 16) >= big
+
+
+def test_reshape_and_cache_rejects(lib):
+    f = lib.pa_reshape_and_cache
+    ok = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, sm=FAKE, t=4, hkv=8, d=128, bs=16, nb=32,
+              dt=ops.PA_BF16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["k"], a["v"], a["kc"], a["vc"], a["sm"], a["t"], a["hkv"], a["d"], a["bs"],
+                 a["nb"], a["dt"], None)
+
+    assert call(t=-1) == ops.PA_EINVAL
+    assert call(hkv=0) == ops.PA_EINVAL
+    assert call(d=80) == ops.PA_EUNSUPPORTED
+    assert call(bs=8) == ops.PA_EUNSUPPORTED
+    assert call(dt=3) == ops.PA_EUNSUPPORTED
+    assert call(sm=None) == ops.PA_EINVAL
+    assert call(t=0, k=None, v=None) == ops.PA_OK      # nothing to append
+
+
+def test_prefill_rejects(lib):
+    f = lib.pa_prefill_chunk
+
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=8, qsl=FAKE, rows=64, cl=FAKE,
+                 s=2, hq=32, hkv=8, d=128, bs=16, nb=64, scale=0.1, dt=ops.PA_BF16)
+        a.update(kw)
+        return f(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mb"], a["qsl"], a["rows"],
+                 a["cl"], a["s"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dt"],
+                 None, 0, None)
+
+    assert call(hq=30) == ops.PA_EINVAL
+    assert call(rows=-1) == ops.PA_EINVAL
+    assert call(d=256) == ops.PA_EUNSUPPORTED
+    assert call(qsl=None) == ops.PA_EINVAL
+    assert call(rows=0, q=None) == ops.PA_OK
