@@ -86,10 +86,10 @@ int pa_reshape_and_cache(const void *key, const void *value,
                          int64_t num_blocks, pa_dtype dtype, void *stream);
 
 /*
- * Bytes of workspace pa_decode needs for these shapes (0 if none).  The result
- * is an upper bound that holds for every context length the block table
- * allows; a workspace of this size can be reused by any later call with the
- * same or smaller shapes.
+ * Bytes of workspace pa_decode needs for these shapes (0 for invalid head
+ * counts).  It does not depend on the context lengths, num_seqs or the block
+ * table width, so one workspace serves every call with the same head counts
+ * and head_dim (or fewer query heads per kv head).
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
@@ -103,10 +103,12 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   out[s,h,:] = sum_t softmax(x)_t * V_t,
  * where token t of s lives in physical block block_tables[s, t / block_size]
  * at offset t % block_size.  n == 0 writes zeros.
- * q, out: [num_seqs, num_q_heads, head_dim].  workspace: device memory of at
- * least pa_decode_workspace_size(...) bytes (may be NULL when that is 0); it
- * holds split-context partial results between the kernels of one call, so
- * calls that overlap in time must not share it.
+ * q, out: [num_seqs, num_q_heads, head_dim].
+ * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
+ * uninitialised is fine.  It carries partial results of contexts split across
+ * waves from the first kernel of the call to the second, so calls that may
+ * overlap in time must not share a workspace.
+ * num_seqs is at most 8192.
  */
 int pa_decode(void *out, const void *q,
               const void *k_cache, const void *v_cache,

@@ -3,6 +3,7 @@
 // Host code only: argument checks (all before anything is enqueued), workspace
 // layout, grid sizing and dispatch to the kernel instances.
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -40,18 +41,56 @@ int heads_per_wave(int group) {
     return gp;
 }
 
-int decode_max_parts(int32_t max_blocks_per_seq) {
-    const long long tokens = (long long)max_blocks_per_seq * 16;
-    return (int)((tokens + pa::kDecodePartTokens - 1) / pa::kDecodePartTokens);
-}
-
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_ws_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
-    const int parts = decode_max_parts(max_blocks_per_seq);
-    if (parts <= 1) return 0;
-    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
-    return align256(rows * 2 * sizeof(float)) + align256(rows * head_dim * sizeof(float));
+// Decode workspace: one split-segment note per wave,
+// then the partial records of up to kDecodeMaxWaves waves (2 slots each):
+// (max, sum) pairs, then accumulators.  Every byte the fix-up kernel reads is
+// written earlier in the same call, so the workspace needs no initialisation.
+struct DecodeWsLayout {
+    size_t split, ml, acc, total;
+};
+
+DecodeWsLayout decode_ws_layout(int gp, int32_t head_dim) {
+    DecodeWsLayout L;
+    const size_t recs = (size_t)pa::kDecodeMaxWaves * 2 * gp;
+    L.split = 0;
+    L.ml = L.split + align256((size_t)pa::kDecodeMaxWaves * sizeof(pa::SplitNote));
+    L.acc = L.ml + align256(recs * 2 * sizeof(float));
+    L.total = L.acc + align256(recs * head_dim * sizeof(float));
+    return L;
+}
+
+int env_int(const char* name, int fallback) {
+    const char* v = getenv(name);
+    if (!v) return fallback;
+    const int x = atoi(v);
+    return x > 0 ? x : fallback;
+}
+
+// Waves of the persistent decode grid: kDecodeWavesPerCU per compute unit of
+// the current device.  PA_DECODE_WAVES overrides the count (launch-shape
+// sweeps and tests); it is read on every call.
+int decode_waves() {
+    static int cached_cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < 64 ? dev : 63;
+    int cus = cached_cus[slot];
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached_cus[slot] = cus;
+    }
+    long long w = (long long)cus * pa::kDecodeWavesPerCU;
+    if (const char* env = getenv("PA_DECODE_WAVES")) {
+        const long long e = atoll(env);
+        if (e > 0) w = e;
+    }
+    if (w > pa::kDecodeMaxWaves) w = pa::kDecodeMaxWaves;
+    w = (w / pa::kDecodeWaves) * pa::kDecodeWaves;
+    if (w < pa::kDecodeWaves) w = pa::kDecodeWaves;
+    return (int)w;
 }
 
 }  // namespace
@@ -89,10 +128,12 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size) {
-    (void)num_kv_heads;
+    (void)max_blocks_per_seq;
     (void)block_size;
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0) return 0;
-    return decode_ws_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq);
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+    if (num_q_heads % num_kv_heads != 0) return 0;
+    const int gp = heads_per_wave(num_q_heads / num_kv_heads);
+    return decode_ws_layout(gp, head_dim).total;
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -111,11 +152,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     if (!isfinite(scale)) return PA_EINVAL;
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
-    const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_EWORKSPACE;
-
+    if (num_seqs > pa::kDecodeMaxSeqs) return PA_EUNSUPPORTED;
     const int group = num_q_heads / num_kv_heads;
     const int gp = heads_per_wave(group);
+    const DecodeWsLayout ws = decode_ws_layout(gp, head_dim);
+    if (workspace == nullptr || workspace_bytes < ws.total) return PA_EWORKSPACE;
+
     pa::DecodeArgs a;
     a.out = out;
     a.q = q;
@@ -123,25 +165,21 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
+    a.ws_split = reinterpret_cast<pa::SplitNote*>(static_cast<char*>(workspace) + ws.split);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml);
+    a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc);
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.group = group;
     a.groups_per_kv = (group + gp - 1) / gp;
-    a.max_parts = decode_max_parts(max_blocks_per_seq);
+    a.n_kvg = num_kv_heads * a.groups_per_kv;
+    a.waves = decode_waves();
     a.scale_log2 = scale * 1.4426950408889634f;
-    const long long grid = (long long)a.max_parts * num_seqs * num_kv_heads * a.groups_per_kv;
-    if (grid > INT32_MAX) return PA_EUNSUPPORTED;
-    if (need > 0) {
-        const size_t rows = (size_t)num_seqs * num_q_heads * a.max_parts;
-        a.ws_ml = static_cast<float*>(workspace);
-        a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * 2 * sizeof(float)));
-    } else {
-        a.ws_ml = nullptr;
-        a.ws_acc = nullptr;
-    }
-    hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, static_cast<hipStream_t>(stream));
+    // PA_DECODE_STAGES (2, 3 or 4) selects the pipeline depth, for sweeps
+    const int stages = env_int("PA_DECODE_STAGES", pa::kDecodeStages);
+    hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 

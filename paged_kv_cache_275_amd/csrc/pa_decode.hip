@@ -8,32 +8,47 @@
 // section 为什么需要推理框架？ (physically scattered blocks).
 //
 // How (MI355X design):
-//  * Work unit = one workgroup of NW waves per (sequence, kv head, head group,
-//    partition of PART = NW*BPW*16 tokens).  Each wave owns BPW consecutive
-//    logical blocks of the partition and ALL query heads (up to GP) that share
-//    the kv head, so every K/V byte is loaded from HBM exactly once and reused
-//    from registers by the whole GQA group.
-//  * Lane layout inside a wave for one 16-token block: lane = 8*tg + dl.
-//    Token group tg (0..7) owns tokens tg and tg+8 of the block, dl (0..7) owns
-//    head_dim/8 consecutive dims.  One token's row of one kv head is
-//    head_dim*elem bytes, read by 8 lanes as 16-byte loads; the loads for a
-//    whole chunk of blocks are issued before any of them is consumed.
-//  * Scores: v_dot2_f32_bf16 partial dot products, then a sum over the 8 lanes
-//    of a token group with three DPP adds.
-//  * Online softmax in the log2 domain with a wave-uniform running max per
-//    head.  The max is only raised when a block holds a score more than
-//    kRescaleSlack above it (a ballot decides, so the branch is uniform): the
-//    result is the same softmax, the rescale of the accumulators becomes rare,
-//    and exp2 never exceeds 2^kRescaleSlack.
-//  * P*V: probabilities packed to bf16 pairs (token tg, token tg+8) and V
-//    re-paired by v_perm so that one v_dot2 adds both tokens' contributions.
-//    The normaliser l is accumulated from the same rounded probabilities.
-//  * End of a work unit: token groups and waves are merged through LDS.  A
-//    sequence that fits one partition is written to out directly; otherwise the
-//    partition's (max, sum, unnormalised acc) go to the workspace and
-//    decode_reduce_kernel merges the partitions (log-sum-exp).
-//  * Tokens >= n in a sequence's last block are masked (score -inf and V
-//    zeroed), so stale slots -- even NaN -- never reach the result.
+//  * Work is flattened into UNITS: one unit = one 16-token block of one
+//    (sequence, kv head, head group) -- its K and V tiles.  Units are ordered
+//    sequence-major, then head group, then block, so consecutive units are
+//    consecutive blocks of one (sequence, head group) SEGMENT.  The U units are
+//    split into W equal contiguous ranges, one per wave of a persistent grid
+//    sized to the chip (stream-K style): every wave streams the same number of
+//    bytes whatever the length mix, so there is no tail of long sequences and
+//    no empty workgroups.
+//  * Each wave owns ALL query heads (up to GP) that share the kv head, so every
+//    K/V byte is read from HBM exactly once and reused from registers by the
+//    whole GQA group.
+//  * Lane layout for one block: lane = 8*tg + dl.  Token group tg (0..7) owns
+//    tokens tg and tg+8.  Each load instruction makes the 8 lanes of a token
+//    group read one contiguous 128-byte line of the token's row (16 bytes per
+//    lane); chunk c of lane dl holds dims c*8*E + dl*E .. +E (E = elements per
+//    16 bytes), so every fetched line is consumed by a single instruction.
+//  * A ring of STAGES blocks is in flight per wave: the loads of unit x+STAGES
+//    are issued as soon as unit x has been consumed (unconditionally, so that
+//    the hardware load counter only has to drain to the stage being consumed).  Block ids (and the valid
+//    token count of each block) are staged per wave in LDS up front, so no load
+//    waits on a block-table read.  The query rows of the next segment are
+//    requested one block before they are needed.
+//  * Scores: v_dot2_f32_bf16 partial dot products, summed over the 8 lanes of
+//    a token group by three DPP adds.  Online softmax in the log2 domain with a
+//    wave-uniform running max per head that is only raised when a block holds
+//    a score more than kRescaleSlack above it (ballot -> uniform branch): the
+//    same softmax, with rare accumulator rescales and exp2 <= 2^kRescaleSlack.
+//  * P*V: probabilities packed to bf16 pairs (token tg, token tg+8); V
+//    re-paired by v_perm so one v_dot2 adds both tokens.  The normaliser is
+//    summed from the same rounded probabilities.
+//  * A segment that one wave covers entirely is normalised and written to out.
+//    A segment split across waves leaves (max, sum, unnormalised acc) records
+//    in the workspace (slot 0: the wave's first segment, slot 1: its last) and
+//    the wave holding its first unit notes it; decode_fixup_kernel then merges
+//    the records of each noted segment (log-sum-exp).  Merging in a second
+//    kernel costs a launch; merging in place would need an agent-scope
+//    release/acquire pair per split segment, which on this chip writes back
+//    and invalidates a whole L2 and measured far slower.
+//  * Tokens >= n in a sequence's last block are masked (score -inf, V zeroed),
+//    so stale slots -- even NaN -- never reach the result.  Sequences with no
+//    tokens get zero rows.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -44,9 +59,13 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: lazy max, exp2 <= 256
 template <typename T, int D>
 struct DecodeGeom {
     static constexpr int kElem = sizeof(T);
-    static constexpr int kDpl = D / 8;                   // dims per lane
-    static constexpr int kVecs = kDpl * kElem / 16;      // 16-byte loads per lane per token
+    static constexpr int kE = 16 / kElem;            // elements per 16-byte chunk
+    static constexpr int kDpl = D / 8;               // dims per lane
+    static constexpr int kVecs = kDpl / kE;          // 16-byte chunks per lane per token
+    static constexpr int kQb = kDpl / 2 > 0 ? kDpl / 2 : 1;
     static_assert(kVecs >= 1, "head_dim too small");
+    // global dim of element j of chunk c of lane dl
+    __device__ static constexpr int dim(int c, int dl, int j) { return c * 8 * kE + dl * kE + j; }
 };
 
 // Scores of the lane's two tokens for its GP heads, fully reduced over dims.
@@ -76,6 +95,31 @@ __device__ __forceinline__ void qk_block(float (&sc)[2][GP], const uint4 (&kr)[2
                 }
             }
             sc[t][g] = sum_lanes8(a);
+        }
+    }
+}
+
+// bf16: acc[g][:] += p0 * V[token 0] + p1 * V[token 1], with (p0, p1) of head g
+// given as a packed bf16 pair pk[g]; l[g] += p0 + p1 as rounded.
+template <int GP, int KDPL, int KVECS>
+__device__ __forceinline__ void pv_block_packed(float (&acc)[GP][KDPL], float (&l)[GP], const uint32_t (&pk)[GP],
+                                                const uint4 (&vr)[2][KVECS]) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g) l[g] = dot2_bf16(pk[g], 0x3F803F80u, l[g]);
+#pragma unroll
+    for (int c = 0; c < KVECS; ++c) {
+        const uint32_t v0[4] = {vr[0][c].x, vr[0][c].y, vr[0][c].z, vr[0][c].w};
+        const uint32_t v1[4] = {vr[1][c].x, vr[1][c].y, vr[1][c].z, vr[1][c].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // (even dim of token 0, even dim of token 1) and the odd dims
+            const uint32_t ev = __builtin_amdgcn_perm(v1[j], v0[j], 0x05040100u);
+            const uint32_t od = __builtin_amdgcn_perm(v1[j], v0[j], 0x07060302u);
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                acc[g][c * 8 + 2 * j] = dot2_bf16(ev, pk[g], acc[g][c * 8 + 2 * j]);
+                acc[g][c * 8 + 2 * j + 1] = dot2_bf16(od, pk[g], acc[g][c * 8 + 2 * j + 1]);
+            }
         }
     }
 }
@@ -126,61 +170,174 @@ __device__ __forceinline__ void pv_block(float (&acc)[GP][KDPL], float (&l)[GP],
     }
 }
 
-template <typename T, int D, int GP, int NW, int BPW, int CH>
-__global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs a) {
+// pref[0] = 0, pref[s+1] = pref[s] + ceil(context_lens[s] / 16), by all
+// NT threads of the workgroup (Hillis-Steele scan of per-thread chunk sums).
+template <int NT>
+__device__ void prefix_blocks(int* pref, int* scratch, const int32_t* __restrict__ ctx, int S) {
+    const int t = threadIdx.x;
+    const int chunk = (S + NT - 1) / NT;
+    const int lo = min(S, t * chunk);
+    const int hi = min(S, lo + chunk);
+    int sum = 0;
+    for (int s = lo; s < hi; ++s) sum += (ctx[s] + kBlockTokens - 1) / kBlockTokens;
+    scratch[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+        const int v = t >= off ? scratch[t - off] : 0;
+        __syncthreads();
+        scratch[t] += v;
+        __syncthreads();
+    }
+    int run = scratch[t] - sum;  // exclusive prefix of this thread's chunk
+    for (int s = lo; s < hi; ++s) {
+        pref[s] = run;
+        run += (ctx[s] + kBlockTokens - 1) / kBlockTokens;
+    }
+    if (t == NT - 1) pref[S] = scratch[t];
+}
+
+// Largest s in [0, S) with n_kvg * pref[s] <= u (u < n_kvg * pref[S]); that
+// sequence has at least one block.
+__device__ __forceinline__ int find_seq(const int* pref, int S, int n_kvg, long long u) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((long long)n_kvg * pref[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Query rows of the GP heads of head group kvg of sequence s, this lane's dims.
+template <typename T, int D, int GP, int KDPL, int KQB>
+__device__ __forceinline__ void load_q(uint32_t (&qb)[GP][KQB], float (&qf)[GP][KDPL], const DecodeArgs& a,
+                                       int s, int kvg, int dl) {
     using G = DecodeGeom<T, D>;
-    constexpr int kDpl = G::kDpl;
-    constexpr int kVecs = G::kVecs;
-    constexpr int kPart = NW * BPW * kBlockTokens;
-    static_assert(BPW % CH == 0, "chunk must divide blocks per wave");
-
-    const int n_kvg = a.num_kv_heads * a.groups_per_kv;
-    const int wg = blockIdx.x;
-    const int kvg = wg % n_kvg;
-    const int rest = wg / n_kvg;
-    const int s = rest % a.num_seqs;
-    const int part = rest / a.num_seqs;
-
-    const int n = a.context_lens[s];
-    const int np = (n + kPart - 1) / kPart;
-    if (part >= (np > 0 ? np : 1)) return;  // uniform over the workgroup
-
     const int hk = kvg / a.groups_per_kv;
-    const int gi0 = (kvg % a.groups_per_kv) * GP;   // first head within the kv head's group
-    const int h0 = hk * a.group + gi0;              // first query head of this unit
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    const int tg = lane >> 3;
-    const int dl = lane & 7;
-
-    // ---- query rows of the GP heads, this lane's dims
-    constexpr int kQb = kDpl / 2 > 0 ? kDpl / 2 : 1;
-    uint32_t qb[GP][kQb];
-    float qf[GP][kDpl];
-    const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + h0) * D + dl * kDpl;
+    const int gi0 = (kvg % a.groups_per_kv) * GP;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + hk * a.group + gi0) * D;
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-        const bool valid = gi0 + g < a.group;
-        if constexpr (sizeof(T) == 2) {
+        // heads past the group (GP > group) reuse the first head's row: their
+        // scores are computed but never stored, and the number of loads issued
+        // does not depend on the group size
+        const int gl = gi0 + g < a.group ? g : 0;
 #pragma unroll
-            for (int c = 0; c < kVecs; ++c) {
-                uint4 v = valid ? *reinterpret_cast<const uint4*>(qrow + (size_t)g * D + c * 8)
-                                : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < G::kVecs; ++c) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qrow + (size_t)gl * D + G::dim(c, dl, 0));
+            if constexpr (sizeof(T) == 2) {
                 qb[g][c * 4 + 0] = v.x; qb[g][c * 4 + 1] = v.y;
                 qb[g][c * 4 + 2] = v.z; qb[g][c * 4 + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < kVecs; ++c) {
-                uint4 v = valid ? *reinterpret_cast<const uint4*>(qrow + (size_t)g * D + c * 4)
-                                : make_uint4(0, 0, 0, 0);
+            } else {
                 qf[g][c * 4 + 0] = __uint_as_float(v.x); qf[g][c * 4 + 1] = __uint_as_float(v.y);
                 qf[g][c * 4 + 2] = __uint_as_float(v.z); qf[g][c * 4 + 3] = __uint_as_float(v.w);
             }
         }
     }
+}
+
+// bf16 query rows as MFMA A operands: lane l holds row l%16 (head gi0 + l%16 of
+// head group kvg; rows past the unit's heads repeat its first head and are
+// never stored) and, for MFMA m, dims 32*m + 8*(l/16) .. +8.
+template <int D, int GP>
+__device__ __forceinline__ void load_q_mfma(uint4 (&qa)[D / 32], const DecodeArgs& a, int s, int kvg, int lane) {
+    const int hk = kvg / a.groups_per_kv;
+    const int gi0 = (kvg % a.groups_per_kv) * GP;
+    const int row = lane & 15;
+    const int hi = (row < GP && gi0 + row < a.group) ? row : 0;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
+                           ((size_t)s * a.num_q_heads + hk * a.group + gi0 + hi) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) qa[m] = *reinterpret_cast<const uint4*>(qrow + 32 * m);
+}
+
+// Range of units [start(w), start(w+1)) of wave w among W waves of U units.
+__device__ __forceinline__ long long range_start(long long w, long long U, long long W) { return w * U / W; }
+
+template <typename T, int D, int GP, int NW, int STAGES, int WIN>
+__global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a) {
+    using G = DecodeGeom<T, D>;
+    constexpr int kDpl = G::kDpl;
+    constexpr int kVecs = G::kVecs;
+    constexpr int kQb = G::kQb;
+    constexpr int kE = G::kE;
+
+    extern __shared__ int smem[];
+    __shared__ int scan_scratch[NW * kWave];
+    const int S = a.num_seqs;
+    int* pref = smem;
+    uint2* tabs = reinterpret_cast<uint2*>(smem + ((S + 1 + 3) & ~3));
+
+    prefix_blocks<NW * kWave>(pref, scan_scratch, a.context_lens, S);
+    __syncthreads();
+    const int n_kvg = a.n_kvg;
+    const long long U = (long long)n_kvg * pref[S];
+    if (blockIdx.x == 0) {
+        // sequences without tokens: their rows are zeros
+        for (int s = 0; s < S; ++s) {
+            if (pref[s + 1] != pref[s]) continue;
+            T* orow = reinterpret_cast<T*>(a.out) + (size_t)s * a.num_q_heads * D;
+            for (int i = threadIdx.x; i < a.num_q_heads * D; i += NW * kWave) orow[i] = T(0);
+        }
+    }
+    const long long W = a.waves;
+    // wave index, made wave-uniform explicitly: everything the wave decides
+    // (ranges, segment walk, branches) derives from it, and the compiler would
+    // otherwise treat threadIdx-derived values as per-lane and turn the whole
+    // control flow into exec-masked vector code
+    const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * NW + threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    // no split segment starts in this wave unless noted below
+    if (lane == 0) a.ws_split[wv].seq = -1;
+    const long long u_begin = range_start(wv, U, W);
+    const long long u_end = range_start(wv + 1, U, W);
+    if (u_begin >= u_end) {
+        // an empty range (fewer units than waves): a zero-weight record in slot 0
+        if (lane < GP) *reinterpret_cast<float2*>(a.ws_ml + ((size_t)wv * 2 * GP + lane) * 2) = make_float2(-INFINITY, 0.f);
+        return;  // wave-uniform; no barrier follows
+    }
+
+    uint2* tab = tabs + (wv % NW) * WIN;
+    const int tg = lane >> 3;
+    const int dl = lane & 7;
+    const int hkv_heads = a.num_kv_heads;
+    const uint32_t lane_off = ((uint32_t)tg * hkv_heads) * D + dl * kE;
+    const uint32_t tok8_off = 8u * hkv_heads * D;
+    const T* kbase = reinterpret_cast<const T*>(a.k_cache);
+    const T* vbase = reinterpret_cast<const T*>(a.v_cache);
+
+    // consume-side position: sequence, head group, block, blocks in sequence
+    int cs = find_seq(pref, S, n_kvg, u_begin);
+    int cnb = pref[cs + 1] - pref[cs];
+    int ckvg, cblk;
+    {
+        const long long r = u_begin - (long long)n_kvg * pref[cs];
+        ckvg = (int)(r / cnb);
+        cblk = (int)(r - (long long)ckvg * cnb);
+    }
+    int seg_first_blk = cblk;
+    bool first_seg = true;
+
+    // bf16: scores come from MFMA.  Lane l holds token l%16 of the block as
+    // MFMA column and the heads 4*(l/16) .. +3 as MFMA rows.
+    constexpr bool kMfma = sizeof(T) == 2;
+    constexpr int kMf = D / 32;        // MFMAs per block
+    constexpr int kRows = (GP + 3) / 4;  // 16-lane row groups that hold heads
+    const int mrow = lane >> 4;
+    const int mtok = lane & 15;
+    const uint32_t kmf_off = ((uint32_t)mtok * hkv_heads) * D + 8 * mrow;
+    uint32_t* lp = reinterpret_cast<uint32_t*>(tabs + NW * WIN) + (wv % NW) * (4 * 8 * 4);
+
+    uint32_t qb[GP][kQb], qnb[GP][kQb];
+    float qf[GP][kDpl], qnf[GP][kDpl];
+    uint4 qa[kMf], qna[kMf];
+    if constexpr (kMfma) {
+        load_q_mfma<D, GP>(qa, a, cs, ckvg, lane);
+    } else {
+        load_q<T, D, GP, kDpl, kQb>(qb, qf, a, cs, ckvg, dl);
+    }
 
     float m[GP], l[GP], acc[GP][kDpl];
+    float mlane[4];  // MFMA layout: running max of the heads of this lane's rows
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
         m[g] = -INFINITY;
@@ -188,244 +345,416 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
 #pragma unroll
         for (int i = 0; i < kDpl; ++i) acc[g][i] = 0.f;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
 
-    const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
-    const int jb_begin = part * (NW * BPW) + w * BPW;
-    const int jb_end = min(jb_begin + BPW, nblk);
-    const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-    const size_t blk_elems = (size_t)kBlockTokens * a.num_kv_heads * D;
-    // element offset of (token tg, kv head hk, lane dims) inside a block
-    const uint32_t lane_off0 = ((uint32_t)tg * a.num_kv_heads + hk) * D + dl * kDpl;
-    const uint32_t tok8_off = 8u * a.num_kv_heads * D;
-    const T* kbase = reinterpret_cast<const T*>(a.k_cache);
-    const T* vbase = reinterpret_cast<const T*>(a.v_cache);
-    constexpr int kElemsPerVec = 16 / sizeof(T);
+    uint4 kr[STAGES][2][kVecs], vr[STAGES][2][kVecs];
+    uint4 kb4[STAGES][kMf];
+    int vld[STAGES];
 
-    for (int jc = jb_begin; jc < jb_end; jc += CH) {
-        uint4 kr[CH][2][kVecs], vr[CH][2][kVecs];
-        // issue every load of the chunk first
+    auto issue = [&](int st, uint2 e) {
+        const uint32_t b = __builtin_amdgcn_readfirstlane(e.x);
+        const uint32_t hv = __builtin_amdgcn_readfirstlane(e.y);
+        vld[st] = (int)(hv >> 16);
+        const size_t base = ((size_t)b * kBlockTokens * hkv_heads + (hv & 0xFFFFu)) * D;
+        const T* vb = vbase + base + lane_off;
+        if constexpr (kMfma) {
+            const T* kb = kbase + base + kmf_off;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            if (jc + i < jb_end) {
-                const int b = bt[jc + i];
-                const T* kb = kbase + (size_t)b * blk_elems + lane_off0;
-                const T* vb = vbase + (size_t)b * blk_elems + lane_off0;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                    for (int c = 0; c < kVecs; ++c) {
-                        kr[i][t][c] = *reinterpret_cast<const uint4*>(kb + t * tok8_off + c * kElemsPerVec);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                    for (int c = 0; c < kVecs; ++c) {
-                        vr[i][t][c] = *reinterpret_cast<const uint4*>(vb + t * tok8_off + c * kElemsPerVec);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int jb = jc + i;
-            if (jb >= jb_end) break;
-            float sc[2][GP];
-            qk_block<T, GP, kDpl, kVecs, kQb>(sc, kr[i], qb, qf);
-            const int tok0 = jb * kBlockTokens + tg;
-            const bool last = (jb + 1) * kBlockTokens > n;  // uniform
+            for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = *reinterpret_cast<const uint4*>(kb + 32 * mm);
+        } else {
+            const T* kb = kbase + base + lane_off;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int g = 0; g < GP; ++g) sc[t][g] *= a.scale_log2;
+                for (int c = 0; c < kVecs; ++c)
+                    kr[st][t][c] = *reinterpret_cast<const uint4*>(kb + t * tok8_off + c * 8 * kE);
             }
-            if (last) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    if (tok0 + 8 * t >= n) {
-#pragma unroll
-                        for (int g = 0; g < GP; ++g) sc[t][g] = -INFINITY;
-#pragma unroll
-                        for (int c = 0; c < kVecs; ++c) vr[i][t][c] = make_uint4(0, 0, 0, 0);
-                    }
-                }
-            }
-            // lazy running max: raise it only when a score clears it by the slack
-            bool need = false;
-#pragma unroll
-            for (int g = 0; g < GP; ++g) need |= fmaxf(sc[0][g], sc[1][g]) > m[g] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-                for (int g = 0; g < GP; ++g) {
-                    const float bm = max_groups8(fmaxf(sc[0][g], sc[1][g]));
-                    const float mn = fmaxf(m[g], bm);
-                    const float alpha = fast_exp2(m[g] - mn);  // 0 when m was -inf
-                    l[g] *= alpha;
-#pragma unroll
-                    for (int d = 0; d < kDpl; ++d) acc[g][d] *= alpha;
-                    m[g] = mn;
-                }
-            }
-            float p[2][GP];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int g = 0; g < GP; ++g) p[t][g] = fast_exp2(sc[t][g] - m[g]);
-            }
-            pv_block<T, GP, kDpl, kVecs>(acc, l, p, vr[i]);
         }
-    }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int c = 0; c < kVecs; ++c)
+                vr[st][t][c] = *reinterpret_cast<const uint4*>(vb + t * tok8_off + c * 8 * kE);
+        }
+    };
 
-    // ---- merge token groups and waves through LDS
-    // token groups tg and tg^1 first (DPP, within a row), then LDS holds 4 per wave
-    __shared__ float sh_acc[NW][4][GP][D];
-    __shared__ float sh_m[NW][GP];
-    __shared__ float sh_l[NW][GP];
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-        const float lt = sum_groups8(l[g]);
-        if (lane == 0) {
-            sh_m[w][g] = m[g];
-            sh_l[w][g] = lt;
-        }
-#pragma unroll
-        for (int d = 0; d < kDpl; ++d) acc[g][d] += dpp_f32<kDppRowRor8>(acc[g][d]);
-    }
-    if ((tg & 1) == 0) {
+    // Segment (cs, ckvg) is done: write its rows, or leave a partial record.
+    auto finish_segment = [&]() {
+        const bool complete = seg_first_blk == 0 && cblk == cnb - 1;
+        const int hk = ckvg / a.groups_per_kv;
+        const int gi0 = (ckvg % a.groups_per_kv) * GP;
+        const int h0 = hk * a.group + gi0;
+        const int slot = first_seg ? 0 : 1;
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
+            const float lt = sum_groups8(l[g]);
 #pragma unroll
-            for (int d = 0; d < kDpl; d += 4) {
-                *reinterpret_cast<float4*>(&sh_acc[w][tg >> 1][g][dl * kDpl + d]) =
-                    make_float4(acc[g][d], acc[g][d + 1], acc[g][d + 2], acc[g][d + 3]);
+            for (int d = 0; d < kDpl; ++d) acc[g][d] = sum_groups8(acc[g][d]);
+            if (tg == 0 && gi0 + g < a.group) {
+                if (complete) {
+                    const float inv = 1.f / lt;
+                    T* orow = reinterpret_cast<T*>(a.out) + ((size_t)cs * a.num_q_heads + h0 + g) * D;
+#pragma unroll
+                    for (int c = 0; c < kVecs; ++c) {
+                        const float* x = &acc[g][c * kE];
+                        if constexpr (sizeof(T) == 2) {
+                            uint4 o;
+                            o.x = pack_bf16x2(x[0] * inv, x[1] * inv);
+                            o.y = pack_bf16x2(x[2] * inv, x[3] * inv);
+                            o.z = pack_bf16x2(x[4] * inv, x[5] * inv);
+                            o.w = pack_bf16x2(x[6] * inv, x[7] * inv);
+                            *reinterpret_cast<uint4*>(orow + G::dim(c, dl, 0)) = o;
+                        } else {
+                            *reinterpret_cast<float4*>(orow + G::dim(c, dl, 0)) =
+                                make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+                        }
+                    }
+                } else {
+                    const size_t rec = ((size_t)wv * 2 + slot) * GP + g;
+                    float* dst = a.ws_acc + rec * D;
+#pragma unroll
+                    for (int c = 0; c < kVecs; ++c) {
+#pragma unroll
+                        for (int j = 0; j < kE; j += 4) {
+                            const float* x = &acc[g][c * kE + j];
+                            *reinterpret_cast<float4*>(dst + G::dim(c, dl, j)) = make_float4(x[0], x[1], x[2], x[3]);
+                        }
+                    }
+                    if (dl == 0) *reinterpret_cast<float2*>(a.ws_ml + rec * 2) = make_float2(m[g], lt);
+                }
             }
+            m[g] = -INFINITY;
+            l[g] = 0.f;
+#pragma unroll
+            for (int d = 0; d < kDpl; ++d) acc[g][d] = 0.f;
         }
-    }
-    __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
+        if (!complete && seg_first_blk == 0 && lane == 0) {
+            // this wave holds the segment's first unit: note it for the fix-up
+            const long long end_unit = (long long)n_kvg * pref[cs] + (long long)ckvg * cnb + cnb;
+            SplitNote sn;
+            sn.seq = cs;
+            sn.kvg = ckvg;
+            sn.last_wave = (int)((end_unit * W - 1) / U);  // wave holding the last unit
+            sn.first_slot = first_seg ? 0 : 1;
+            a.ws_split[wv] = sn;
+        }
+        first_seg = false;
+    };
 
-    const bool single = np <= 1;
-    const size_t ws_row0 = ((size_t)s * a.num_q_heads + h0) * a.max_parts + part;
-    for (int idx = threadIdx.x; idx < GP * D; idx += NW * kWave) {
-        const int g = idx / D;
-        const int d = idx % D;
-        if (gi0 + g >= a.group) continue;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sh_m[ww][g]);
-        float L = 0.f, A = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float sw = (sh_m[ww][g] == -INFINITY) ? 0.f : fast_exp2(sh_m[ww][g] - mx);
-            L += sh_l[ww][g] * sw;
-            A += (sh_acc[ww][0][g][d] + sh_acc[ww][1][g][d] + sh_acc[ww][2][g][d] +
-                  sh_acc[ww][3][g][d]) * sw;
+    for (long long wb0 = u_begin; wb0 < u_end; wb0 += WIN) {
+        const int wn = (int)min((long long)WIN, u_end - wb0);
+        // ---- stage this window's block ids and valid-token counts in LDS
+        for (int i = lane; i < wn; i += kWave) {
+            const long long u = wb0 + i;
+            const int s = find_seq(pref, S, n_kvg, u);
+            const int nb = pref[s + 1] - pref[s];
+            const long long r = u - (long long)n_kvg * pref[s];
+            const int kvg = (int)(r / nb);
+            const int blk = (int)(r - (long long)kvg * nb);
+            const int b = a.block_tables[(size_t)s * a.max_blocks_per_seq + blk];
+            const int n = a.context_lens[s];
+            const int valid = min(kBlockTokens, n - blk * kBlockTokens);
+            tab[i] = make_uint2((uint32_t)b, (uint32_t)(kvg / a.groups_per_kv) | ((uint32_t)valid << 16));
         }
-        if (single) {
-            const float o = L > 0.f ? A / L : 0.f;
-            T* orow = reinterpret_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h0 + g) * D;
-            if constexpr (sizeof(T) == 2) {
-                reinterpret_cast<uint16_t*>(orow)[d] = f32_to_bf16_bits(o);
-            } else {
-                reinterpret_cast<float*>(orow)[d] = o;
-            }
-        } else {
-            const size_t row = ws_row0 + (size_t)g * a.max_parts;
-            a.ws_acc[row * D + d] = A;
-            if (d == 0) {
-                a.ws_ml[row * 2 + 0] = mx;
-                a.ws_ml[row * 2 + 1] = L;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // Every stage is (re)filled on every path -- past the window end with a
+        // repeat of its last unit, never consumed -- and scheduling barriers keep
+        // each stage's loads together and in ring order.  The number of loads in
+        // flight is then the same on all paths, and the compiler's wait counts
+        // only wait for the stage being consumed, not for the whole ring.
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st) {
+            issue(st, tab[min(st, wn - 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int x = 0; x < wn; x += STAGES) {
+#pragma unroll
+            for (int st = 0; st < STAGES; ++st) {
+                const int ux = x + st;
+                if (ux >= wn) break;
+                const long long ug = wb0 + ux;
+                const bool seg_end = (cblk == cnb - 1) || (ug == u_end - 1);
+                const bool has_next = seg_end && (ug + 1 < u_end);
+                int ns = cs, nkvg = ckvg;
+                if (has_next) {
+                    nkvg = ckvg + 1;
+                    if (nkvg == n_kvg) {
+                        nkvg = 0;
+                        ++ns;
+                        while (pref[ns + 1] == pref[ns]) ++ns;
+                    }
+                    if constexpr (kMfma) {
+                        load_q_mfma<D, GP>(qna, a, ns, nkvg, lane);
+                    } else {
+                        load_q<T, D, GP, kDpl, kQb>(qnb, qnf, a, ns, nkvg, dl);
+                    }
+                }
+
+                const int valid = vld[st];
+                if (valid < kBlockTokens) {
+                    // stale slots past the context: zero their V (may hold NaN)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        if (tg + 8 * t >= valid) {
+#pragma unroll
+                            for (int c = 0; c < kVecs; ++c) vr[st][t][c] = make_uint4(0, 0, 0, 0);
+                        }
+                    }
+                }
+                if constexpr (kMfma) {
+                    // ---- scores: S[head][token] = Q K^T on the matrix cores
+                    f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qa[mm], kb4[st][mm], s4);
+                    float sv[4];
+                    bool need = false;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        sv[r] = mtok < valid ? s4[r] * a.scale_log2 : -INFINITY;
+                        need |= (4 * mrow + r < GP) && sv[r] > mlane[r] + kRescaleSlack;
+                    }
+                    // ---- lazy running max (rare, uniform branch)
+                    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                        float bm4[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) bm4[r] = max_row16(sv[r]);
+#pragma unroll
+                        for (int g = 0; g < GP; ++g) {
+                            const float bm = readlane_f32(bm4[g % 4], 16 * (g / 4));
+                            const float mn = fmaxf(m[g], bm);
+                            const float alpha = fast_exp2(m[g] - mn);  // 0 when m was -inf
+                            l[g] *= alpha;
+#pragma unroll
+                            for (int d = 0; d < kDpl; ++d) acc[g][d] *= alpha;
+                            m[g] = mn;
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            float v = m[r < GP ? r : 0];
+#pragma unroll
+                            for (int rg = 1; rg < kRows; ++rg) {
+                                if (4 * rg + r < GP && mrow == rg) v = m[4 * rg + r];
+                            }
+                            mlane[r] = v;
+                        }
+                    }
+                    // ---- probabilities, paired (token t, token t+8), to the P*V layout
+                    uint32_t pk4[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float pr = fast_exp2(sv[r] - mlane[r]);
+                        pk4[r] = pack_bf16x2(pr, dpp_f32<kDppRowRor8>(pr));
+                    }
+                    if (mtok < 8 && mrow < kRows) {
+                        *reinterpret_cast<uint4*>(lp + (mrow * 8 + mtok) * 4) = make_uint4(pk4[0], pk4[1], pk4[2], pk4[3]);
+                    }
+                    uint32_t pk[GP];
+#pragma unroll
+                    for (int rg = 0; rg < kRows; ++rg) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(lp + (rg * 8 + tg) * 4);
+                        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (4 * rg + r < GP) pk[4 * rg + r] = vv[r];
+                        }
+                    }
+                    pv_block_packed<GP, kDpl, kVecs>(acc, l, pk, vr[st]);
+                } else {
+                    // ---- scores of this block
+                    float sc[2][GP];
+                    qk_block<T, GP, kDpl, kVecs, kQb>(sc, kr[st], qb, qf);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                        for (int g = 0; g < GP; ++g) sc[t][g] = tg + 8 * t < valid ? sc[t][g] * a.scale_log2 : -INFINITY;
+                    }
+                    // ---- lazy running max, probabilities, P*V
+                    bool need = false;
+#pragma unroll
+                    for (int g = 0; g < GP; ++g) need |= fmaxf(sc[0][g], sc[1][g]) > m[g] + kRescaleSlack;
+                    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+                        for (int g = 0; g < GP; ++g) {
+                            const float bm = max_groups8(fmaxf(sc[0][g], sc[1][g]));
+                            const float mn = fmaxf(m[g], bm);
+                            const float alpha = fast_exp2(m[g] - mn);  // 0 when m was -inf
+                            l[g] *= alpha;
+#pragma unroll
+                            for (int d = 0; d < kDpl; ++d) acc[g][d] *= alpha;
+                            m[g] = mn;
+                        }
+                    }
+                    float p[2][GP];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                        for (int g = 0; g < GP; ++g) p[t][g] = fast_exp2(sc[t][g] - m[g]);
+                    }
+                    pv_block<T, GP, kDpl, kVecs>(acc, l, p, vr[st]);
+                }
+
+                // ---- refill this stage (unconditionally, see above)
+                __builtin_amdgcn_sched_barrier(0);
+                issue(st, tab[min(ux + STAGES, wn - 1)]);
+                __builtin_amdgcn_sched_barrier(0);
+
+                if (!seg_end) {
+                    ++cblk;
+                    continue;
+                }
+                finish_segment();
+                if (has_next) {
+                    cs = ns;
+                    ckvg = nkvg;
+                    cblk = 0;
+                    cnb = pref[cs + 1] - pref[cs];
+                    seg_first_blk = 0;
+                    if constexpr (kMfma) {
+#pragma unroll
+                        for (int mm = 0; mm < kMf; ++mm) qa[mm] = qna[mm];
+                    } else {
+#pragma unroll
+                        for (int g = 0; g < GP; ++g) {
+#pragma unroll
+                            for (int i = 0; i < kQb; ++i) qb[g][i] = qnb[g][i];
+#pragma unroll
+                            for (int i = 0; i < kDpl; ++i) qf[g][i] = qnf[g][i];
+                        }
+                    }
+                }
             }
         }
     }
 }
 
-// Merge the partitions of every (sequence, query head) whose context spans more
-// than one partition: M = max_p m_p, L = sum_p l_p 2^(m_p - M),
-// out = sum_p acc_p 2^(m_p - M) / L.  One wave per (sequence, head).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a, int part_tokens) {
-    const int wave_id = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (wave_id >= a.num_seqs * a.num_q_heads) return;
+// Merge the partial records of the split segment noted by wave w (if any):
+//   M = max_v m_v,  L = sum_v l_v 2^(m_v - M),  out = sum_v acc_v 2^(m_v - M) / L
+// over the waves v = w .. last_wave that hold its units.  One workgroup per
+// noting wave, one wave per head; every record load is independent of the
+// others, so a merge costs two dependent memory round trips (the note, then
+// the records).
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) {
+    const int w = blockIdx.x;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
-    const int s = wave_id / a.num_q_heads;
-    const int h = wave_id % a.num_q_heads;
-    const int n = a.context_lens[s];
-    const int np = (n + part_tokens - 1) / part_tokens;
-    if (np <= 1) return;
-    const size_t row0 = ((size_t)s * a.num_q_heads + h) * a.max_parts;
-    float mx = -INFINITY;
-    for (int p = lane; p < np; p += kWave) mx = fmaxf(mx, a.ws_ml[(row0 + p) * 2]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float L = 0.f;
-    for (int p = lane; p < np; p += kWave) {
-        L += a.ws_ml[(row0 + p) * 2 + 1] * fast_exp2(a.ws_ml[(row0 + p) * 2] - mx);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    const SplitNote sn = a.ws_split[w];
+    if (sn.seq < 0) return;
+    const int nrec = sn.last_wave - w + 1;
+    const int gi0 = (sn.kvg % a.groups_per_kv) * GP;
+    const int hk = sn.kvg / a.groups_per_kv;
     constexpr int kPerLane = D / kWave;  // 1 or 2
-    float A[kPerLane];
+    constexpr int kBatch = 8;
+    auto rec_of = [&](int j, int g) -> size_t {  // record of wave w + j, head g
+        return ((size_t)(w + j) * 2 + (j == 0 ? sn.first_slot : 0)) * GP + g;
+    };
+    {
+        if (gi0 + g >= a.group) return;
+        // lane j: (max, sum) of record j (chunks of 64 records)
+        float M = -INFINITY;
+        for (int j = lane; j < nrec; j += kWave) M = fmaxf(M, a.ws_ml[rec_of(j, g) * 2]);
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) A[i] = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float sw = fast_exp2(a.ws_ml[(row0 + p) * 2] - mx);
-        const float* src = a.ws_acc + (row0 + p) * D + lane * kPerLane;
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        float L = 0.f;
+        float o[kPerLane];
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) A[i] += src[i] * sw;
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    T* orow = reinterpret_cast<T*>(a.out) + ((size_t)s * a.num_q_heads + h) * D + lane * kPerLane;
+        for (int i = 0; i < kPerLane; ++i) o[i] = 0.f;
+        for (int j0 = 0; j0 < nrec; j0 += kWave) {
+            float swj = 0.f, lj = 0.f;
+            if (j0 + lane < nrec) {
+                const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + rec_of(j0 + lane, g) * 2);
+                swj = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
+                lj = ml.y;
+            }
+            L += lj * swj;
+            const int cnt = min(kWave, nrec - j0);
+            for (int b0 = 0; b0 < cnt; b0 += kBatch) {
+                float x[kBatch][kPerLane];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        const float o = A[i] * inv;
-        if constexpr (sizeof(T) == 2) {
-            reinterpret_cast<uint16_t*>(orow)[i] = f32_to_bf16_bits(o);
-        } else {
-            reinterpret_cast<float*>(orow)[i] = o;
+                for (int b = 0; b < kBatch; ++b) {
+                    const bool ok = b0 + b < cnt;
+                    const size_t r = rec_of(ok ? j0 + b0 + b : 0, g);
+#pragma unroll
+                    for (int i = 0; i < kPerLane; ++i) x[b][i] = a.ws_acc[r * D + lane * kPerLane + i];
+                }
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) {
+                    const float sw = __shfl(swj, (b0 + b) & (kWave - 1));
+                    if (b0 + b < cnt && sw != 0.f) {
+#pragma unroll
+                        for (int i = 0; i < kPerLane; ++i) o[i] += x[b][i] * sw;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+        const float inv = 1.f / L;
+        T* orow = reinterpret_cast<T*>(a.out) + ((size_t)sn.seq * a.num_q_heads + hk * a.group + gi0 + g) * D +
+                  lane * kPerLane;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            if constexpr (sizeof(T) == 2) {
+                reinterpret_cast<uint16_t*>(orow)[i] = f32_to_bf16_bits(o[i] * inv);
+            } else {
+                reinterpret_cast<float*>(orow)[i] = o[i] * inv;
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T, int D, int GP, int NW, int BPW, int CH>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    constexpr int kPart = NW * BPW * kBlockTokens;
-    const long long grid = (long long)a.max_parts * a.num_seqs * a.num_kv_heads * a.groups_per_kv;
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, GP, NW, BPW, CH>), dim3((unsigned)grid),
-                       dim3(NW * kWave), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.max_parts > 1) {
-        const int waves = a.num_seqs * a.num_q_heads;
-        hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3((waves + 3) / 4), dim3(256), 0, stream,
-                           a, kPart);
-        e = hipGetLastError();
-    }
-    return e;
+size_t decode_stream_lds_bytes(int num_seqs) {
+    return (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int) +
+           (size_t)kDecodeWaves * kDecodeWindow * sizeof(uint2) +
+           (size_t)kDecodeWaves * 4 * 8 * 4 * sizeof(uint32_t);
+}
+
+template <typename T, int D, int GP, int STAGES>
+static hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream) {
+    const size_t lds = decode_stream_lds_bytes(a.num_seqs);
+    hipLaunchKernelGGL((decode_stream_kernel<T, D, GP, kDecodeWaves, STAGES, kDecodeWindow>),
+                       dim3(a.waves / kDecodeWaves), dim3(kDecodeWaves * kWave), lds, stream, a);
+    return hipGetLastError();
 }
 
 template <typename T, int D, int GP>
-static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
-    return launch_decode_t<T, D, GP, kDecodeWaves, kDecodeBlocksPerWave, kDecodeChunk>(a, stream);
+static hipError_t launch_decode_g(const DecodeArgs& a, int stages, hipStream_t stream) {
+    hipError_t e;
+    switch (stages) {
+        case 2: e = launch_stream<T, D, GP, 2>(a, stream); break;
+        case 3: e = launch_stream<T, D, GP, 3>(a, stream); break;
+        default: e = launch_stream<T, D, GP, 4>(a, stream); break;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_fixup_kernel<T, D, GP>), dim3(a.waves), dim3(GP * kWave), 0, stream, a);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_d(const DecodeArgs& a, int gp, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int stages, hipStream_t stream) {
     switch (gp) {
-        case 1: return launch_decode_g<T, D, 1>(a, stream);
-        case 2: return launch_decode_g<T, D, 2>(a, stream);
-        case 4: return launch_decode_g<T, D, 4>(a, stream);
-        default: return launch_decode_g<T, D, 8>(a, stream);
+        case 1: return launch_decode_g<T, D, 1>(a, stages, stream);
+        case 2: return launch_decode_g<T, D, 2>(a, stages, stream);
+        case 4: return launch_decode_g<T, D, 4>(a, stages, stream);
+        default: return launch_decode_g<T, D, 8>(a, stages, stream);
     }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages,
+                         hipStream_t stream) {
     if (dtype_bf16) {
-        return head_dim == 64 ? launch_decode_d<uint16_t, 64>(a, gp, stream)
-                              : launch_decode_d<uint16_t, 128>(a, gp, stream);
+        return head_dim == 64 ? launch_decode_d<uint16_t, 64>(a, gp, stages, stream)
+                              : launch_decode_d<uint16_t, 128>(a, gp, stages, stream);
     }
-    return head_dim == 64 ? launch_decode_d<float, 64>(a, gp, stream)
-                          : launch_decode_d<float, 128>(a, gp, stream);
+    return head_dim == 64 ? launch_decode_d<float, 64>(a, gp, stages, stream)
+                          : launch_decode_d<float, 128>(a, gp, stages, stream);
 }
 
 }  // namespace pa

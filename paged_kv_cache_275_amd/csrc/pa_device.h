@@ -14,12 +14,17 @@ constexpr int kBlockTokens = 16;  // tokens per KV block
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // DPP controls (row = 16 lanes).
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
 constexpr int kDppRowRor8 = 0x128;     // lane i <- lane (i+8) mod 16 within a row
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor2 = 0x122;
+constexpr int kDppRowRor1 = 0x121;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -60,6 +65,27 @@ __device__ __forceinline__ float sum_groups8(float x) {
         x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
     return x;
+}
+
+// Max over the 16 lanes of each row (every lane of the row gets it).
+__device__ __forceinline__ float max_row16(float x) {
+    x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+    x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+    x = fmaxf(x, dpp_f32<kDppRowRor2>(x));
+    x = fmaxf(x, dpp_f32<kDppRowRor1>(x));
+    return x;
+}
+
+__device__ __forceinline__ float readlane_f32(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// D[16x16] += A[16x32] * B[32x16] in bf16 with fp32 accumulation.  Lane l holds
+// A row l%16 and B column l%16, k-slots 8*(l/16) .. +8 (8 bf16 in 16 bytes);
+// it receives D column l%16, rows 4*(l/16) .. +3.
+__device__ __forceinline__ f32x4_t mfma16x16x32_bf16(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

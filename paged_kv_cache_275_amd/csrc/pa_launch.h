@@ -6,13 +6,28 @@
 
 namespace pa {
 
-// Decode work split: a workgroup of kDecodeWaves waves covers one partition of
-// kDecodeWaves * kDecodeBlocksPerWave blocks of one sequence; each wave issues
-// the loads of kDecodeChunk blocks before consuming them.
+// Decode launch shape: a persistent grid of waves (kDecodeWaves per
+// workgroup), each streaming an equal share of the (sequence, head group,
+// block) units with kDecodeStages blocks in flight; block ids are staged in
+// LDS kDecodeWindow units at a time.
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeBlocksPerWave = 4;
-constexpr int kDecodeChunk = 2;
-constexpr int kDecodePartTokens = kDecodeWaves * kDecodeBlocksPerWave * 16;
+constexpr int kDecodeStages = 4;      // default; 2 and 3 are also built
+constexpr int kDecodeWindow = 512;
+constexpr int kDecodeWavesPerCU = 4;
+constexpr int kDecodeMaxWaves = 4096;   // workspace records are sized for this many waves
+constexpr int kDecodeMaxSeqs = 8192;    // sequence prefix sums live in LDS
+
+// A segment (sequence, head group) whose units were split across waves, noted
+// by the wave that holds its first unit.  seq < 0: no split segment starts in
+// that wave.  The segment's records are slot first_slot of the noting wave and
+// slot 0 of every later wave up to last_wave (waves with an empty range leave a
+// record of zero weight there).
+struct SplitNote {
+    int seq;
+    int kvg;
+    int last_wave;
+    int first_slot;
+};
 
 struct DecodeArgs {
     void* out;
@@ -21,19 +36,23 @@ struct DecodeArgs {
     const void* v_cache;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    float* ws_ml;   // [S, Hq, max_parts, 2]  (running max in log2 units, sum)
-    float* ws_acc;  // [S, Hq, max_parts, D]  unnormalised partial outputs
+    SplitNote* ws_split;   // [waves] split segment starting in each wave
+    float* ws_ml;   // [waves, 2, GP, 2]  (running max in log2 units, sum)
+    float* ws_acc;  // [waves, 2, GP, D]  unnormalised partial outputs
     int max_blocks_per_seq;
     int num_seqs;
     int num_q_heads;
     int num_kv_heads;
     int group;          // query heads per kv head
     int groups_per_kv;  // head groups (of up to GP heads) per kv head
-    int max_parts;      // partitions per sequence the workspace holds
+    int n_kvg;          // num_kv_heads * groups_per_kv
+    int waves;          // waves in the persistent grid (multiple of kDecodeWaves)
     float scale_log2;   // scale * log2(e)
 };
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, hipStream_t stream);
+size_t decode_stream_lds_bytes(int num_seqs);
+hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages,
+                         hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int num_tokens, int row_bytes,

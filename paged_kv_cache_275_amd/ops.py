@@ -126,7 +126,7 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blo
 
 
 def decode_workspace(q, k_cache, block_tables):
-    """Allocate (torch, uint8) a workspace big enough for decode() with these shapes."""
+    """Allocate a workspace (torch, uint8) big enough for decode() with these shapes."""
     import torch
     n = decode_workspace_size(q.shape[0], q.shape[1], k_cache.shape[2], q.shape[2],
                               block_tables.shape[1], k_cache.shape[1])

@@ -63,8 +63,9 @@ def _decode(lib, **kw):
     (dict(scale=float("nan")), ops.PA_EINVAL),
     (dict(q=None), ops.PA_EINVAL),
     (dict(bt=None), ops.PA_EINVAL),
-    (dict(mb=4096, ws=None), ops.PA_EWORKSPACE),
-    (dict(mb=4096, ws_bytes=16), ops.PA_EWORKSPACE),
+    (dict(ws=None), ops.PA_EWORKSPACE),
+    (dict(ws_bytes=16), ops.PA_EWORKSPACE),
+    (dict(s=8193), ops.PA_EUNSUPPORTED),
 ])
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
@@ -75,14 +76,13 @@ def test_decode_empty_batch_is_noop(lib):
 
 
 def test_decode_workspace_size(lib):
-    # short tables fit one partition: no workspace
-    assert lib.pa_decode_workspace_size(128, 32, 8, 128, 4, 16) == 0
-    big = lib.pa_decode_workspace_size(16, 16, 8, 128, 4096, 16)
-    assert big > 0
-    # monotone in every shape argument
-    assert lib.pa_decode_workspace_size(32, 16, 8, 128, 4096, 16) >= big
-    assert lib.pa_decode_workspace_size(16, 32, 8, 128, 4096, 16) >= big
-    assert lib.pa_decode_workspace_size(16, 16, 8, 128, 8192, 16) >= big
+    small = lib.pa_decode_workspace_size(128, 32, 8, 128, 4, 16)
+    assert small > 0                                   # prefix sums + partial records
+    # monotone in the shape arguments that size it; independent of the table width
+    assert lib.pa_decode_workspace_size(256, 32, 8, 128, 4, 16) >= small
+    assert lib.pa_decode_workspace_size(128, 64, 8, 128, 4, 16) >= small
+    assert lib.pa_decode_workspace_size(128, 32, 8, 128, 4096, 16) == small
+    assert lib.pa_decode_workspace_size(128, 30, 8, 128, 4, 16) == 0   # invalid heads
 
 
 def test_reshape_and_cache_rejects(lib):

@@ -156,3 +156,15 @@ def test_invalid_arguments_raise():
     with pytest.raises(ops.PAError) as e:
         ops.decode(torch.empty_like(q), q, kc, kc, bt, cl, 0.1)   # 6 % 4 != 0
     assert e.value.status == ops.PA_EINVAL
+
+
+@pytest.mark.parametrize("waves", ["4", "8", "60", "4096"])
+def test_decode_launch_shapes(waves, monkeypatch):
+    """The result must not depend on how the units are split over waves: one
+    workgroup (several LDS windows per wave), few waves, an odd count and the
+    largest grid (mostly empty ranges)."""
+    monkeypatch.setenv("PA_DECODE_WAVES", waves)
+    wl = W.make_workload("llama3_8b", seed=21, num_seqs=12)
+    _check_workload(wl, f"waves={waves}")
+    wl = W.make_workload("long_skewed", seed=22, num_seqs=2)
+    _check_workload(wl, f"waves={waves}/long")
