@@ -197,7 +197,8 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                      float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
                      void* stream) {
-    (void)workspace; (void)workspace_bytes; (void)stream;
+    (void)workspace;
+    (void)workspace_bytes;
     int rc = check_dtype(dtype);
     if (rc) return rc;
     if (num_seqs < 0 || total_query_rows < 0) return PA_EINVAL;
@@ -210,7 +211,27 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
     if (num_seqs == 0 || total_query_rows == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
         return PA_EINVAL;
-    return PA_EUNSUPPORTED;
+    if (dtype != PA_BF16) return PA_EUNSUPPORTED;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > pa::kPrefillMaxGroup) return PA_EUNSUPPORTED;
+    int gp = 1;
+    while (gp < group) gp *= 2;
+    pa::PrefillArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.query_start_loc = query_start_loc;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipError_t e = pa::launch_prefill(a, head_dim, total_query_rows, gp, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
 }  // extern "C"

@@ -51,6 +51,27 @@ struct DecodeArgs {
 };
 
 size_t decode_stream_lds_bytes(int num_seqs);
+
+struct PrefillArgs {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* query_start_loc;
+    const int32_t* context_lens;
+    int max_blocks_per_seq;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;          // query heads per kv head
+    float scale_log2;   // scale * log2(e)
+};
+
+// Query heads per prefill column group: a power of two >= group, at most 16.
+constexpr int kPrefillMaxGroup = 16;
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages,
                          hipStream_t stream);
 
