@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "pa.h"
 #include "pa_launch.h"
 
@@ -61,11 +63,12 @@ DecodeWsLayout decode_ws_layout(int gp, int32_t head_dim) {
     return L;
 }
 
-int env_int(const char* name, int fallback) {
+// Integer from the environment if set and >= lo, else fallback.
+int env_int(const char* name, int fallback, int lo = 1) {
     const char* v = getenv(name);
     if (!v) return fallback;
     const int x = atoi(v);
-    return x > 0 ? x : fallback;
+    return x >= lo ? x : fallback;
 }
 
 // Waves of the persistent decode grid: kDecodeWavesPerCU per compute unit of
@@ -175,7 +178,14 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.group = group;
     a.groups_per_kv = (group + gp - 1) / gp;
     a.n_kvg = num_kv_heads * a.groups_per_kv;
-    a.waves = decode_waves();
+    // wave groups of n_kvg waves (one per head group), as many as fit the
+    // persistent grid and the workspace records
+    a.wave_groups = std::max(1, std::min(decode_waves(), pa::kDecodeMaxWaves) / a.n_kvg);
+    if ((long long)a.wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
+    a.waves = a.wave_groups * a.n_kvg;
+    // PA_DECODE_SWITCH_TICKS (0..64) overrides the segment cost, for sweeps
+    a.unit_ticks = pa::kDecodeUnitTicks;
+    a.switch_ticks = std::min(64, env_int("PA_DECODE_SWITCH_TICKS", pa::kDecodeSwitchTicks, 0));
     a.scale_log2 = scale * 1.4426950408889634f;
     // PA_DECODE_STAGES (2, 3 or 4) selects the pipeline depth, for sweeps
     const int stages = env_int("PA_DECODE_STAGES", pa::kDecodeStages);

@@ -8,14 +8,19 @@
 // section 为什么需要推理框架？ (physically scattered blocks).
 //
 // How (MI355X design):
-//  * Work is flattened into UNITS: one unit = one 16-token block of one
-//    (sequence, kv head, head group) -- its K and V tiles.  Units are ordered
-//    sequence-major, then head group, then block, so consecutive units are
-//    consecutive blocks of one (sequence, head group) SEGMENT.  The U units are
-//    split into W equal contiguous ranges, one per wave of a persistent grid
-//    sized to the chip (stream-K style): every wave streams the same number of
-//    bytes whatever the length mix, so there is no tail of long sequences and
-//    no empty workgroups.
+//  * A UNIT is one 16-token block of one (sequence, head group): the K and V
+//    rows of one kv head in that block.  The persistent grid (sized to the
+//    chip) is cut into wave GROUPS of n_kvg waves; wave kvg of a group owns head
+//    group kvg.  The blocks of all sequences, concatenated, are split into one
+//    contiguous range per group (stream-K style), and every wave of the group
+//    streams that range for its head group.  So the waves of a group read the
+//    kv heads of a block at about the same time -- whole 2 KB token rows, one
+//    DRAM page each -- instead of one 256-byte head slice per page opening, and
+//    every wave streams the same number of bytes whatever the length mix.
+//    The split is measured in ticks: a block costs unit_ticks and each
+//    sequence in a range adds switch_ticks for closing its segment, so waves
+//    with many short sequences get fewer blocks.  Consecutive units of a wave
+//    are consecutive blocks of one (sequence, head group) SEGMENT.
 //  * Each wave owns ALL query heads (up to GP) that share the kv head, so every
 //    K/V byte is read from HBM exactly once and reused from registers by the
 //    whole GQA group.
@@ -28,8 +33,10 @@
 //    are issued as soon as unit x has been consumed (unconditionally, so that
 //    the hardware load counter only has to drain to the stage being consumed).  Block ids (and the valid
 //    token count of each block) are staged per wave in LDS up front, so no load
-//    waits on a block-table read.  The query rows of the next segment are
-//    requested one block before they are needed.
+//    waits on a block-table read.  Each block's query rows are loaded with its
+//    K/V (bf16 path): hardware load counters drain in issue order, so a query
+//    load issued outside the ring would force the whole ring to land at every
+//    switch of segment.
 //  * Scores: v_dot2_f32_bf16 partial dot products, summed over the 8 lanes of
 //    a token group by three DPP adds.  Online softmax in the log2 domain with a
 //    wave-uniform running max per head that is only raised when a block holds
@@ -170,30 +177,122 @@ __device__ __forceinline__ void pv_block(float (&acc)[GP][KDPL], float (&l)[GP],
     }
 }
 
-// pref[0] = 0, pref[s+1] = pref[s] + ceil(context_lens[s] / 16), by all
-// NT threads of the workgroup (Hillis-Steele scan of per-thread chunk sums).
+// Reduce-scatter over the 8 token groups (lane bits 3..5) of the lane's
+// V = GP*KDPL partial sums, flat index g*KDPL + d.  Each halving step hands
+// half of the values to the partner lane and adds what comes back (the
+// permlane swaps exchange the upper 32 / odd 16-lane rows of their first
+// operand with the lower / even rows of the second), so lane tg ends with the
+// complete sums of flat values tg*V/8 .. tg*V/8 + V/8 - 1: 7V/8 exchanges
+// instead of 3V for a full all-reduce.
+template <int GP, int KDPL>
+__device__ __forceinline__ void reduce_scatter8(float (&red)[GP * KDPL / 8], const float (&acc)[GP][KDPL],
+                                                int lane) {
+    constexpr int V = GP * KDPL;
+    static_assert(V % 8 == 0, "reduce-scatter needs 8 | GP*KDPL");
+    float h1[V / 2];
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+        const int j = i + V / 2;
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i / KDPL][i % KDPL]),
+                                                        __float_as_uint(acc[j / KDPL][j % KDPL]), false, false);
+        h1[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    float h2[V / 4];
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(h1[i]), __float_as_uint(h1[i + V / 4]),
+                                                        false, false);
+        h2[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const bool up8 = (lane & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < V / 8; ++i) {
+        const float keep = up8 ? h2[i + V / 8] : h2[i];
+        const float send = up8 ? h2[i] : h2[i + V / 8];
+        red[i] = keep + dpp_f32<kDppRowRor8>(send);
+    }
+}
+
+// Store P consecutive values (times mul) to dst, converted to OutT.
+template <typename OutT, int P>
+__device__ __forceinline__ void store_piece(OutT* dst, const float* v, float mul) {
+    if constexpr (sizeof(OutT) == 2) {
+        if constexpr (P == 8) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0] * mul, v[1] * mul), pack_bf16x2(v[2] * mul, v[3] * mul),
+                                                        pack_bf16x2(v[4] * mul, v[5] * mul), pack_bf16x2(v[6] * mul, v[7] * mul));
+        } else if constexpr (P == 4) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0] * mul, v[1] * mul), pack_bf16x2(v[2] * mul, v[3] * mul));
+        } else if constexpr (P == 2) {
+            *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0] * mul, v[1] * mul);
+        } else {
+            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_bits(v[0] * mul);
+        }
+    } else {
+        if constexpr (P == 4) {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul);
+        } else if constexpr (P == 2) {
+            *reinterpret_cast<float2*>(dst) = make_float2(v[0] * mul, v[1] * mul);
+        } else {
+            *reinterpret_cast<float*>(dst) = v[0] * mul;
+        }
+    }
+}
+
+// Store the lane's CH reduced values, elements d0 .. d0+CH-1 of its KDPL dims
+// (element d of lane dl is dim (d/KE)*8*KE + dl*KE + d%KE), into row dst.
+template <typename OutT, int KE, int CH>
+__device__ __forceinline__ void store_run(OutT* dst, const float (&v)[CH], float mul, int d0, int dl) {
+    constexpr int kRun = CH < KE ? CH : KE;                        // contiguous dims
+    constexpr int kMaxP = 16 / (int)sizeof(OutT);
+    constexpr int P = kRun < kMaxP ? kRun : kMaxP;                 // per store
+#pragma unroll
+    for (int i = 0; i < CH; i += P) {
+        const int d = d0 + i;
+        store_piece<OutT, P>(dst + (d / KE) * 8 * KE + dl * KE + d % KE, &v[i], mul);
+    }
+}
+
+// Work is measured in TICKS: every unit costs unit_ticks, and every segment
+// adds switch_ticks for the work of closing it (reduction, stores, a fresh
+// running max).  pref[s] = blocks of sequences before s and tpref[s] = ticks of
+// one head group of every sequence before s, computed by all NT threads of the
+// workgroup (Hillis-Steele scan of per-thread chunk sums).
 template <int NT>
-__device__ void prefix_blocks(int* pref, int* scratch, const int32_t* __restrict__ ctx, int S) {
+__device__ void prefix_blocks(int* pref, int* tpref, int2* scratch, const int32_t* __restrict__ ctx, int S,
+                              int unit_ticks, int switch_ticks) {
     const int t = threadIdx.x;
     const int chunk = (S + NT - 1) / NT;
     const int lo = min(S, t * chunk);
     const int hi = min(S, lo + chunk);
-    int sum = 0;
-    for (int s = lo; s < hi; ++s) sum += (ctx[s] + kBlockTokens - 1) / kBlockTokens;
+    auto nblk = [&](int s) { return (ctx[s] + kBlockTokens - 1) / kBlockTokens; };
+    auto ticks = [&](int nb) { return nb * unit_ticks + (nb > 0 ? switch_ticks : 0); };
+    int2 sum = make_int2(0, 0);
+    for (int s = lo; s < hi; ++s) {
+        const int nb = nblk(s);
+        sum.x += nb;
+        sum.y += ticks(nb);
+    }
     scratch[t] = sum;
     __syncthreads();
     for (int off = 1; off < NT; off <<= 1) {
-        const int v = t >= off ? scratch[t - off] : 0;
+        const int2 v = t >= off ? scratch[t - off] : make_int2(0, 0);
         __syncthreads();
-        scratch[t] += v;
+        scratch[t].x += v.x;
+        scratch[t].y += v.y;
         __syncthreads();
     }
-    int run = scratch[t] - sum;  // exclusive prefix of this thread's chunk
+    int2 run = make_int2(scratch[t].x - sum.x, scratch[t].y - sum.y);  // exclusive prefix of the chunk
     for (int s = lo; s < hi; ++s) {
-        pref[s] = run;
-        run += (ctx[s] + kBlockTokens - 1) / kBlockTokens;
+        pref[s] = run.x;
+        tpref[s] = run.y;
+        const int nb = nblk(s);
+        run.x += nb;
+        run.y += ticks(nb);
     }
-    if (t == NT - 1) pref[S] = scratch[t];
+    if (t == NT - 1) {
+        pref[S] = scratch[t].x;
+        tpref[S] = scratch[t].y;
+    }
 }
 
 // Largest s in [0, S) with n_kvg * pref[s] <= u (u < n_kvg * pref[S]); that
@@ -235,23 +334,21 @@ __device__ __forceinline__ void load_q(uint32_t (&qb)[GP][KQB], float (&qf)[GP][
     }
 }
 
-// bf16 query rows as MFMA A operands: lane l holds row l%16 (head gi0 + l%16 of
-// head group kvg; rows past the unit's heads repeat its first head and are
-// never stored) and, for MFMA m, dims 32*m + 8*(l/16) .. +8.
-template <int D, int GP>
-__device__ __forceinline__ void load_q_mfma(uint4 (&qa)[D / 32], const DecodeArgs& a, int s, int kvg, int lane) {
-    const int hk = kvg / a.groups_per_kv;
-    const int gi0 = (kvg % a.groups_per_kv) * GP;
-    const int row = lane & 15;
-    const int hi = (row < GP && gi0 + row < a.group) ? row : 0;
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((size_t)s * a.num_q_heads + hk * a.group + gi0 + hi) * D + 8 * (lane >> 4);
-#pragma unroll
-    for (int m = 0; m < D / 32; ++m) qa[m] = *reinterpret_cast<const uint4*>(qrow + 32 * m);
-}
+// Range of ticks [start(g), start(g+1)) of wave group g among G groups of T
+// ticks.  Tick t lies in the range of group ((t + 1) * G - 1) / T.
+__device__ __forceinline__ long long range_start(long long g, long long T, long long G) { return g * T / G; }
 
-// Range of units [start(w), start(w+1)) of wave w among W waves of U units.
-__device__ __forceinline__ long long range_start(long long w, long long U, long long W) { return w * U / W; }
+// Index (into the concatenated blocks of all sequences) of the first block
+// whose first tick is >= t, T ticks in all.  Block blk of sequence s starts at
+// tick tpref[s] + blk * R.
+__device__ __forceinline__ int block_at_tick(long long t, long long T, const int* pref, const int* tpref, int S,
+                                             int R) {
+    if (t >= T) return pref[S];
+    const int s = find_seq(tpref, S, 1, t);
+    const int nb = pref[s + 1] - pref[s];
+    const int r = (int)(t - tpref[s]);
+    return pref[s] + min((r + R - 1) / R, nb);
+}
 
 template <typename T, int D, int GP, int NW, int STAGES, int WIN>
 __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a) {
@@ -262,41 +359,58 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     constexpr int kE = G::kE;
 
     extern __shared__ int smem[];
-    __shared__ int scan_scratch[NW * kWave];
+    __shared__ int2 scan_scratch[NW * kWave];
     const int S = a.num_seqs;
     int* pref = smem;
-    uint2* tabs = reinterpret_cast<uint2*>(smem + ((S + 1 + 3) & ~3));
+    int* tpref = smem + ((S + 1 + 3) & ~3);
+    uint4* tabs = reinterpret_cast<uint4*>(smem + 2 * ((S + 1 + 3) & ~3));
 
-    prefix_blocks<NW * kWave>(pref, scan_scratch, a.context_lens, S);
+    const int R = a.unit_ticks;
+    const int C = a.switch_ticks;
+    prefix_blocks<NW * kWave>(pref, tpref, scan_scratch, a.context_lens, S, R, C);
     __syncthreads();
     const int n_kvg = a.n_kvg;
-    const long long U = (long long)n_kvg * pref[S];
-    if (blockIdx.x == 0) {
-        // sequences without tokens: their rows are zeros
-        for (int s = 0; s < S; ++s) {
-            if (pref[s + 1] != pref[s]) continue;
-            T* orow = reinterpret_cast<T*>(a.out) + (size_t)s * a.num_q_heads * D;
-            for (int i = threadIdx.x; i < a.num_q_heads * D; i += NW * kWave) orow[i] = T(0);
+    const long long TT = tpref[S];  // ticks of one head group over all sequences
+    if (threadIdx.x < kWave) {
+        // sequences without tokens get zero rows: wave 0 of every workgroup
+        // checks 64 sequences at a time, one per lane
+        for (int s0 = blockIdx.x * kWave; s0 < S; s0 += gridDim.x * kWave) {
+            const int sl = s0 + (int)threadIdx.x;
+            uint64_t em = __builtin_amdgcn_ballot_w64(sl < S && pref[min(sl, S - 1) + 1] == pref[min(sl, S - 1)]);
+            while (em != 0) {
+                const int j = __builtin_ctzll(em);
+                em &= em - 1;
+                T* orow = reinterpret_cast<T*>(a.out) + (size_t)(s0 + j) * a.num_q_heads * D;
+                for (int i = threadIdx.x; i < a.num_q_heads * D; i += kWave) orow[i] = T(0);
+            }
         }
     }
-    const long long W = a.waves;
+    const long long NG = a.wave_groups;
     // wave index, made wave-uniform explicitly: everything the wave decides
     // (ranges, segment walk, branches) derives from it, and the compiler would
     // otherwise treat threadIdx-derived values as per-lane and turn the whole
     // control flow into exec-masked vector code
     const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * NW + threadIdx.x / kWave);
+    if (wv >= a.waves) return;  // padding waves of the last workgroup (no barrier follows)
     const int lane = threadIdx.x & (kWave - 1);
     // no split segment starts in this wave unless noted below
     if (lane == 0) a.ws_split[wv].seq = -1;
-    const long long u_begin = range_start(wv, U, W);
-    const long long u_end = range_start(wv + 1, U, W);
+    const int kvg = wv % n_kvg;                  // this wave's head group
+    const long long grp = wv / n_kvg;            // its wave group
+    const int hk = kvg / a.groups_per_kv;        // kv head
+    const int gi0 = (kvg % a.groups_per_kv) * GP;  // first query head of the group within the kv head
+    const int h0 = hk * a.group + gi0;           // ... among all query heads
+    const int nvh = min(GP, a.group - gi0);      // query heads present (the last group may hold fewer)
+    const int u_begin = block_at_tick(range_start(grp, TT, NG), TT, pref, tpref, S, R);
+    const int u_end = block_at_tick(range_start(grp + 1, TT, NG), TT, pref, tpref, S, R);
     if (u_begin >= u_end) {
-        // an empty range (fewer units than waves): a zero-weight record in slot 0
+        // an empty range (a share smaller than a unit): a zero-weight record in
+        // slot 0, in case the wave lies inside a split segment's span of waves
         if (lane < GP) *reinterpret_cast<float2*>(a.ws_ml + ((size_t)wv * 2 * GP + lane) * 2) = make_float2(-INFINITY, 0.f);
         return;  // wave-uniform; no barrier follows
     }
 
-    uint2* tab = tabs + (wv % NW) * WIN;
+    uint4* tab = tabs + (wv % NW) * WIN;
     const int tg = lane >> 3;
     const int dl = lane & 7;
     const int hkv_heads = a.num_kv_heads;
@@ -305,15 +419,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     const T* kbase = reinterpret_cast<const T*>(a.k_cache);
     const T* vbase = reinterpret_cast<const T*>(a.v_cache);
 
-    // consume-side position: sequence, head group, block, blocks in sequence
-    int cs = find_seq(pref, S, n_kvg, u_begin);
+    // consume-side position: sequence, block, blocks in sequence
+    int cs = find_seq(pref, S, 1, u_begin);
     int cnb = pref[cs + 1] - pref[cs];
-    int ckvg, cblk;
-    {
-        const long long r = u_begin - (long long)n_kvg * pref[cs];
-        ckvg = (int)(r / cnb);
-        cblk = (int)(r - (long long)ckvg * cnb);
-    }
+    int cblk = u_begin - pref[cs];
     int seg_first_blk = cblk;
     bool first_seg = true;
 
@@ -329,12 +438,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 
     uint32_t qb[GP][kQb], qnb[GP][kQb];
     float qf[GP][kDpl], qnf[GP][kDpl];
-    uint4 qa[kMf], qna[kMf];
-    if constexpr (kMfma) {
-        load_q_mfma<D, GP>(qa, a, cs, ckvg, lane);
-    } else {
-        load_q<T, D, GP, kDpl, kQb>(qb, qf, a, cs, ckvg, dl);
-    }
+    if constexpr (!kMfma) load_q<T, D, GP, kDpl, kQb>(qb, qf, a, cs, kvg, dl);
 
     float m[GP], l[GP], acc[GP][kDpl];
     float mlane[4];  // MFMA layout: running max of the heads of this lane's rows
@@ -349,10 +453,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
 
     uint4 kr[STAGES][2][kVecs], vr[STAGES][2][kVecs];
-    uint4 kb4[STAGES][kMf];
+    uint4 kb4[STAGES][kMf], qs[STAGES][kMf];
     int vld[STAGES];
 
-    auto issue = [&](int st, uint2 e) {
+    auto issue = [&](int st, uint4 e) {
         const uint32_t b = __builtin_amdgcn_readfirstlane(e.x);
         const uint32_t hv = __builtin_amdgcn_readfirstlane(e.y);
         vld[st] = (int)(hv >> 16);
@@ -362,6 +466,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             const T* kb = kbase + base + kmf_off;
 #pragma unroll
             for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = *reinterpret_cast<const uint4*>(kb + 32 * mm);
+            // the unit's query rows travel with its K/V: no load outside the ring
+            // ever has to be waited for (loads complete in issue order)
+            const uint32_t qrow0 = __builtin_amdgcn_readfirstlane(e.z);
+            const uint32_t nvh = __builtin_amdgcn_readfirstlane(e.w);
+            const uint32_t hi = (uint32_t)mtok < nvh ? (uint32_t)mtok : 0u;
+            const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)(qrow0 + hi) * D + 8 * mrow;
+#pragma unroll
+            for (int mm = 0; mm < kMf; ++mm) qs[st][mm] = *reinterpret_cast<const uint4*>(qp + 32 * mm);
         } else {
             const T* kb = kbase + base + lane_off;
 #pragma unroll
@@ -379,51 +491,39 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         }
     };
 
-    // Segment (cs, ckvg) is done: write its rows, or leave a partial record.
+    // Segment (cs, kvg) is done: write its rows, or leave a partial record.
+    // The partial sums are reduce-scattered over the token groups, so lane
+    // (tg, dl) ends with kCh complete sums of one head: elements d0 .. d0+kCh-1
+    // of its dims of head gl.
     auto finish_segment = [&]() {
+        constexpr int kCh = GP * kDpl / 8;
         const bool complete = seg_first_blk == 0 && cblk == cnb - 1;
-        const int hk = ckvg / a.groups_per_kv;
-        const int gi0 = (ckvg % a.groups_per_kv) * GP;
-        const int h0 = hk * a.group + gi0;
         const int slot = first_seg ? 0 : 1;
+        float red[kCh];
+        reduce_scatter8<GP, kDpl>(red, acc, lane);
+        const int gl = (tg * kCh) / kDpl;
+        const int d0 = (tg * kCh) % kDpl;
+        float mg = m[0], lg = sum_groups8(l[0]);
+#pragma unroll
+        for (int g = 1; g < GP; ++g) {
+            const float lt = sum_groups8(l[g]);
+            if (gl == g) {
+                mg = m[g];
+                lg = lt;
+            }
+        }
+        if (gi0 + gl < a.group) {
+            if (complete) {
+                T* orow = reinterpret_cast<T*>(a.out) + ((size_t)cs * a.num_q_heads + h0 + gl) * D;
+                store_run<T, kE, kCh>(orow, red, 1.f / lg, d0, dl);
+            } else {
+                const size_t rec = ((size_t)wv * 2 + slot) * GP + gl;
+                store_run<float, kE, kCh>(a.ws_acc + rec * D, red, 1.f, d0, dl);
+                if (dl == 0 && d0 == 0) *reinterpret_cast<float2*>(a.ws_ml + rec * 2) = make_float2(mg, lg);
+            }
+        }
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-            const float lt = sum_groups8(l[g]);
-#pragma unroll
-            for (int d = 0; d < kDpl; ++d) acc[g][d] = sum_groups8(acc[g][d]);
-            if (tg == 0 && gi0 + g < a.group) {
-                if (complete) {
-                    const float inv = 1.f / lt;
-                    T* orow = reinterpret_cast<T*>(a.out) + ((size_t)cs * a.num_q_heads + h0 + g) * D;
-#pragma unroll
-                    for (int c = 0; c < kVecs; ++c) {
-                        const float* x = &acc[g][c * kE];
-                        if constexpr (sizeof(T) == 2) {
-                            uint4 o;
-                            o.x = pack_bf16x2(x[0] * inv, x[1] * inv);
-                            o.y = pack_bf16x2(x[2] * inv, x[3] * inv);
-                            o.z = pack_bf16x2(x[4] * inv, x[5] * inv);
-                            o.w = pack_bf16x2(x[6] * inv, x[7] * inv);
-                            *reinterpret_cast<uint4*>(orow + G::dim(c, dl, 0)) = o;
-                        } else {
-                            *reinterpret_cast<float4*>(orow + G::dim(c, dl, 0)) =
-                                make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
-                        }
-                    }
-                } else {
-                    const size_t rec = ((size_t)wv * 2 + slot) * GP + g;
-                    float* dst = a.ws_acc + rec * D;
-#pragma unroll
-                    for (int c = 0; c < kVecs; ++c) {
-#pragma unroll
-                        for (int j = 0; j < kE; j += 4) {
-                            const float* x = &acc[g][c * kE + j];
-                            *reinterpret_cast<float4*>(dst + G::dim(c, dl, j)) = make_float4(x[0], x[1], x[2], x[3]);
-                        }
-                    }
-                    if (dl == 0) *reinterpret_cast<float2*>(a.ws_ml + rec * 2) = make_float2(m[g], lt);
-                }
-            }
             m[g] = -INFINITY;
             l[g] = 0.f;
 #pragma unroll
@@ -432,32 +532,33 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
         if (!complete && seg_first_blk == 0 && lane == 0) {
-            // this wave holds the segment's first unit: note it for the fix-up
-            const long long end_unit = (long long)n_kvg * pref[cs] + (long long)ckvg * cnb + cnb;
+            // this wave holds the segment's first unit: note it for the fix-up,
+            // with the wave (same head group) whose group holds the first tick
+            // of the segment's last block
+            const long long t_last = (long long)tpref[cs] + (long long)(cnb - 1) * R;
             SplitNote sn;
             sn.seq = cs;
-            sn.kvg = ckvg;
-            sn.last_wave = (int)((end_unit * W - 1) / U);  // wave holding the last unit
+            sn.kvg = kvg;
+            sn.last_wave = (int)(((t_last + 1) * NG - 1) / TT) * n_kvg + kvg;
             sn.first_slot = first_seg ? 0 : 1;
             a.ws_split[wv] = sn;
         }
         first_seg = false;
     };
 
-    for (long long wb0 = u_begin; wb0 < u_end; wb0 += WIN) {
-        const int wn = (int)min((long long)WIN, u_end - wb0);
+    for (int wb0 = u_begin; wb0 < u_end; wb0 += WIN) {
+        const int wn = min(WIN, u_end - wb0);
         // ---- stage this window's block ids and valid-token counts in LDS
         for (int i = lane; i < wn; i += kWave) {
-            const long long u = wb0 + i;
-            const int s = find_seq(pref, S, n_kvg, u);
-            const int nb = pref[s + 1] - pref[s];
-            const long long r = u - (long long)n_kvg * pref[s];
-            const int kvg = (int)(r / nb);
-            const int blk = (int)(r - (long long)kvg * nb);
+            const int u = wb0 + i;
+            const int s = find_seq(pref, S, 1, u);
+            const int blk = u - pref[s];
             const int b = a.block_tables[(size_t)s * a.max_blocks_per_seq + blk];
-            const int n = a.context_lens[s];
-            const int valid = min(kBlockTokens, n - blk * kBlockTokens);
-            tab[i] = make_uint2((uint32_t)b, (uint32_t)(kvg / a.groups_per_kv) | ((uint32_t)valid << 16));
+            const int valid = min(kBlockTokens, a.context_lens[s] - blk * kBlockTokens);
+            // block id; kv head | valid tokens << 16; first query row of the
+            // head group; query heads present
+            tab[i] = make_uint4((uint32_t)b, (uint32_t)hk | ((uint32_t)valid << 16),
+                                (uint32_t)(s * a.num_q_heads + h0), (uint32_t)nvh);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -478,22 +579,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             for (int st = 0; st < STAGES; ++st) {
                 const int ux = x + st;
                 if (ux >= wn) break;
-                const long long ug = wb0 + ux;
+                const int ug = wb0 + ux;
                 const bool seg_end = (cblk == cnb - 1) || (ug == u_end - 1);
                 const bool has_next = seg_end && (ug + 1 < u_end);
-                int ns = cs, nkvg = ckvg;
+                int ns = cs;
                 if (has_next) {
-                    nkvg = ckvg + 1;
-                    if (nkvg == n_kvg) {
-                        nkvg = 0;
-                        ++ns;
-                        while (pref[ns + 1] == pref[ns]) ++ns;
-                    }
-                    if constexpr (kMfma) {
-                        load_q_mfma<D, GP>(qna, a, ns, nkvg, lane);
-                    } else {
-                        load_q<T, D, GP, kDpl, kQb>(qnb, qnf, a, ns, nkvg, dl);
-                    }
+                    ++ns;
+                    while (pref[ns + 1] == pref[ns]) ++ns;
+                    if constexpr (!kMfma) load_q<T, D, GP, kDpl, kQb>(qnb, qnf, a, ns, kvg, dl);
                 }
 
                 const int valid = vld[st];
@@ -511,7 +604,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                     // ---- scores: S[head][token] = Q K^T on the matrix cores
                     f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qa[mm], kb4[st][mm], s4);
+                    for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qs[st][mm], kb4[st][mm], s4);
                     float sv[4];
                     bool need = false;
 #pragma unroll
@@ -611,14 +704,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                 finish_segment();
                 if (has_next) {
                     cs = ns;
-                    ckvg = nkvg;
                     cblk = 0;
                     cnb = pref[cs + 1] - pref[cs];
                     seg_first_blk = 0;
-                    if constexpr (kMfma) {
-#pragma unroll
-                        for (int mm = 0; mm < kMf; ++mm) qa[mm] = qna[mm];
-                    } else {
+                    if constexpr (!kMfma) {
 #pragma unroll
                         for (int g = 0; g < GP; ++g) {
 #pragma unroll
@@ -635,7 +724,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 
 // Merge the partial records of the split segment noted by wave w (if any):
 //   M = max_v m_v,  L = sum_v l_v 2^(m_v - M),  out = sum_v acc_v 2^(m_v - M) / L
-// over the waves v = w .. last_wave that hold its units.  One workgroup per
+// over the waves v = w, w + n_kvg, ..., last_wave (the waves of the segment's
+// head group in consecutive wave groups) that hold its units.  One workgroup per
 // noting wave, one wave per head; every record load is independent of the
 // others, so a merge costs two dependent memory round trips (the note, then
 // the records).
@@ -646,13 +736,13 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
     const int lane = threadIdx.x & (kWave - 1);
     const SplitNote sn = a.ws_split[w];
     if (sn.seq < 0) return;
-    const int nrec = sn.last_wave - w + 1;
+    const int nrec = (sn.last_wave - w) / a.n_kvg + 1;  // waves w, w + n_kvg, ..., last_wave
     const int gi0 = (sn.kvg % a.groups_per_kv) * GP;
     const int hk = sn.kvg / a.groups_per_kv;
     constexpr int kPerLane = D / kWave;  // 1 or 2
     constexpr int kBatch = 8;
-    auto rec_of = [&](int j, int g) -> size_t {  // record of wave w + j, head g
-        return ((size_t)(w + j) * 2 + (j == 0 ? sn.first_slot : 0)) * GP + g;
+    auto rec_of = [&](int j, int g) -> size_t {  // record of wave w + j * n_kvg, head g
+        return ((size_t)(w + j * a.n_kvg) * 2 + (j == 0 ? sn.first_slot : 0)) * GP + g;
     };
     {
         if (gi0 + g >= a.group) return;
@@ -711,8 +801,8 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
 
 // ---------------------------------------------------------------- launchers
 size_t decode_stream_lds_bytes(int num_seqs) {
-    return (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int) +
-           (size_t)kDecodeWaves * kDecodeWindow * sizeof(uint2) +
+    return 2 * (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int) +
+           (size_t)kDecodeWaves * kDecodeWindow * sizeof(uint4) +
            (size_t)kDecodeWaves * 4 * 8 * 4 * sizeof(uint32_t);
 }
 
@@ -720,7 +810,7 @@ template <typename T, int D, int GP, int STAGES>
 static hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream) {
     const size_t lds = decode_stream_lds_bytes(a.num_seqs);
     hipLaunchKernelGGL((decode_stream_kernel<T, D, GP, kDecodeWaves, STAGES, kDecodeWindow>),
-                       dim3(a.waves / kDecodeWaves), dim3(kDecodeWaves * kWave), lds, stream, a);
+                       dim3((a.waves + kDecodeWaves - 1) / kDecodeWaves), dim3(kDecodeWaves * kWave), lds, stream, a);
     return hipGetLastError();
 }
 

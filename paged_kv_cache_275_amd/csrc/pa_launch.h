@@ -12,16 +12,22 @@ namespace pa {
 // LDS kDecodeWindow units at a time.
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeStages = 4;      // default; 2 and 3 are also built
-constexpr int kDecodeWindow = 512;
+constexpr int kDecodeWindow = 256;
 constexpr int kDecodeWavesPerCU = 4;
 constexpr int kDecodeMaxWaves = 4096;   // workspace records are sized for this many waves
 constexpr int kDecodeMaxSeqs = 8192;    // sequence prefix sums live in LDS
+// Work-split costs: closing a segment takes about as long as streaming one
+// unit, so each segment counts kDecodeSwitchTicks / kDecodeUnitTicks extra
+// units when the units are shared out among the waves.
+constexpr int kDecodeUnitTicks = 4;
+constexpr int kDecodeSwitchTicks = 4;
 
 // A segment (sequence, head group) whose units were split across waves, noted
 // by the wave that holds its first unit.  seq < 0: no split segment starts in
 // that wave.  The segment's records are slot first_slot of the noting wave and
-// slot 0 of every later wave up to last_wave (waves with an empty range leave a
-// record of zero weight there).
+// slot 0 of the waves of the same head group in the following wave groups
+// (every n_kvg-th wave) up to last_wave; waves with an empty range leave a
+// record of zero weight there.
 struct SplitNote {
     int seq;
     int kvg;
@@ -46,7 +52,10 @@ struct DecodeArgs {
     int group;          // query heads per kv head
     int groups_per_kv;  // head groups (of up to GP heads) per kv head
     int n_kvg;          // num_kv_heads * groups_per_kv
-    int waves;          // waves in the persistent grid (multiple of kDecodeWaves)
+    int waves;          // working waves: wave_groups * n_kvg (the grid is rounded up to whole workgroups)
+    int wave_groups;    // groups of n_kvg waves; group g streams the g-th share of all blocks
+    int unit_ticks;     // work-split cost of one unit (one block of one head group)
+    int switch_ticks;   // extra cost of closing a segment (one head group of a sequence)
     float scale_log2;   // scale * log2(e)
 };
 
