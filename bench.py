@@ -1,19 +1,29 @@
-"""Benchmark: one paged-attention decode step (KV append + decode) on one MI355X.
+"""Benchmark: one paged-attention step (KV append + decode) on one MI355X.
 
 A step is one pass of the hot path over one batch: pa_reshape_and_cache of
 the new tokens, then pa_decode over every sequence (and, for the mixed
-workload, pa_prefill_chunk over the prefill chunks).  Inputs are the seeded
-synthetic workloads of paged_kv_cache_275_amd.workloads, resident in HBM before
-timing starts.  To time HBM rather than the 256 MB Infinity Cache, the step
-rotates over R independent copies of the KV pool, so each step's K/V was last
-touched R-1 steps (GBs of traffic) earlier.
+workload, pa_prefill_chunk over the prefill chunks first).  Inputs are the
+seeded synthetic workloads of paged_kv_cache_275_amd.workloads, resident in
+HBM before timing starts.  To time HBM rather than the 256 MB Infinity Cache,
+the step rotates over R independent copies of the KV pool, so each step's K/V
+was last touched R-1 steps (GBs of traffic) earlier.
 
-Prints ONE JSON line.  value = effective KV bandwidth of the step (decode KV
-bytes / step time, GB/s); us_per_step is reported next to it.
+Prints ONE JSON line.  value = effective KV bandwidth of the whole step
+(decode KV bytes / step wall time, GB/s); us_per_step sits next to it.
+roofline = the kernel with the largest average duration, timed with HIP
+events on the stream it runs on; its traffic comes from a committed
+rocprofv3 counter summary (profiles/) when that summary was taken on the
+kernel's current source, else null.
+
+Other modes (for the profiling summaries under profiles/):
+  --copy-calibration   a plain 512 MiB device copy, to scale HBM counters
+  --summarize-pmc ...  turn rocprofv3 counter CSVs into a traffic summary
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -23,8 +33,48 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+METRIC = "paged-attn decode \u00b5s/step + effective KV GB/s (% HBM peak), Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
-MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+CALIB_BYTES = 512 << 20      # size of the plain copy used to scale HBM counters
+
+# Sources the streaming decode kernel is compiled from: a traffic summary is
+# valid only for the exact bytes it was measured on.
+KERNEL_SOURCES = {
+    "decode_stream_kernel": ["pa_decode.hip", "pa_device.h", "pa_launch.h"],
+    "prefill_kernel": ["pa_prefill.hip", "pa_device.h", "pa_launch.h"],
+}
+CSRC = os.path.join(ROOT, "paged_kv_cache_275_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_summary_path(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per dispatch from the committed counter summary, or None when
+    there is none or it was taken on other kernel sources."""
+    path = traffic_summary_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != source_hash(kernel):
+        return None
+    return float(kv["hbm_bytes_per_dispatch"])
 
 
 def _to_dev(a, dev):
@@ -76,6 +126,79 @@ def cpu_baseline(wl, budget_s: float):
     }
 
 
+def prefill_flops(wl) -> int:
+    """Algorithmic flops of the prefill chunks: 4*D per (query head, causal pair)."""
+    p = wl.prefill
+    pairs = 0
+    for s in range(len(p.context_lens)):
+        c = int(p.query_start_loc[s + 1] - p.query_start_loc[s])
+        n = int(p.context_lens[s])
+        pairs += sum(n - c + i + 1 for i in range(c))
+    return 4 * wl.head_dim * wl.num_q_heads * pairs
+
+
+def copy_calibration():
+    """A plain device-to-device copy of CALIB_BYTES, three times, for counter scaling."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": CALIB_BYTES, "copies": 3}), flush=True)
+
+
+def _pmc_rows(path, counter, name_part):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                rows.append(float(r["Counter_Value"]))
+    return rows
+
+
+def summarize_pmc(args):
+    """Write profiles/<kernel>_<workload>_traffic.txt from four rocprofv3 --pmc CSVs."""
+    import statistics
+    fetch = _pmc_rows(args.pmc_fetch, "FETCH_SIZE", args.kernel)
+    write = _pmc_rows(args.pmc_write, "WRITE_SIZE", args.kernel)
+    cfetch = max(_pmc_rows(args.calib_fetch, "FETCH_SIZE", "copyBuffer"))
+    cwrite = max(_pmc_rows(args.calib_write, "WRITE_SIZE", "copyBuffer"))
+    if not fetch or not write:
+        raise SystemExit(f"no {args.kernel} dispatches in the counter files")
+    ff = CALIB_BYTES / (cfetch * 1024.0)
+    wf = CALIB_BYTES / (cwrite * 1024.0)
+    f_kib, w_kib = statistics.median(fetch), statistics.median(write)
+    total = f_kib * 1024.0 * ff + w_kib * 1024.0 * wf
+    lines = [
+        f"# HBM traffic of {args.kernel} on the {args.workload} workload (rocprofv3 --pmc)",
+        "# Counters are KiB per dispatch, median over the dispatches of the run.  Each is",
+        f"# scaled by (bytes / counter) of a plain {CALIB_BYTES >> 20} MiB device copy, which reads",
+        "# and writes exactly that many bytes.",
+        "# Commands, from the repository root:",
+        *[f"#   {c}" for c in args.commands.split(";;")],
+        f"kernel = {args.kernel}",
+        f"workload = {args.workload}",
+        f"kernel_source_sha256 = {source_hash(args.kernel)}",
+        f"dispatches_fetch = {len(fetch)}",
+        f"dispatches_write = {len(write)}",
+        f"fetch_size_kib_per_dispatch = {f_kib:.1f}",
+        f"write_size_kib_per_dispatch = {w_kib:.1f}",
+        f"copy_fetch_size_kib = {cfetch:.1f}",
+        f"copy_write_size_kib = {cwrite:.1f}",
+        f"copy_fetch_factor = {ff:.4f}",
+        f"copy_write_factor = {wf:.4f}",
+        f"hbm_bytes_per_dispatch = {total:.0f}",
+    ]
+    if args.algorithmic_bytes:
+        lines.append(f"algorithmic_bytes_per_dispatch = {args.algorithmic_bytes}")
+        lines.append(f"traffic_over_algorithmic = {total / float(args.algorithmic_bytes):.4f}")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,12 +208,29 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="independent KV pool copies")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", action="store_true")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--calib-fetch")
+    ap.add_argument("--calib-write")
+    ap.add_argument("--kernel", default="decode_stream_kernel")
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--algorithmic-bytes", type=int, default=0)
+    ap.add_argument("--commands", default="")
+    ap.add_argument("--out")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the paged-attention path here has no "
-              "multi-GPU mode (see the sharding note in DESIGN.md); use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this paged-attention path has no multi-GPU "
+              "mode (how it would shard is described in DESIGN.md); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -122,42 +262,102 @@ def main():
         pre["out"] = torch.empty_like(pre["q"])
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
-        kc, vc = pools[i % len(pools)]
-        if ev is not None:
+    # arguments are checked once per pool copy; the loop only crosses the C ABI
+    calls = []
+    for kc, vc in pools:
+        calls.append({
+            "append": ops.bind_reshape_and_cache(k_new, v_new, kc, vc, slots),
+            "prefill": None if pre is None else ops.bind_prefill_chunk(
+                pre["out"], pre["q"], kc, vc, pre["bt"], pre["qsl"], pre["cl"], wl.scale),
+            "decode": ops.bind_decode(out, q, kc, vc, bt, cl, wl.scale, workspace=ws),
+        })
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)   # creates the HIP event, so its handle can go to the library
+        return evs
+
+    # ev: call boundaries (append | prefill | decode) or None; kev: the decode
+    # streaming kernel's start / stop, set by the library from its dispatch
+    def step(i, ev=None, kev=None):
+        c = calls[i % len(calls)]
+        if ev is not None and ev[0] is not None:
             ev[0].record(stream)
-        ops.reshape_and_cache(k_new, v_new, kc, vc, slots)
-        if ev is not None:
+        c["append"]()
+        if ev is not None and ev[1] is not None:
             ev[1].record(stream)
-        if pre is not None:
-            ops.prefill_chunk(pre["out"], pre["q"], kc, vc, pre["bt"], pre["qsl"], pre["cl"], wl.scale)
-        if ev is not None:
+        if c["prefill"] is not None:
+            c["prefill"]()
+        if ev is not None and ev[2] is not None:
             ev[2].record(stream)
-        ops.decode(out, q, kc, vc, bt, cl, wl.scale, workspace=ws)
-        if ev is not None:
+        c["decode"](None if kev is None else (kev[0].cuda_event, kev[1].cuda_event))
+        if ev is not None and ev[3] is not None:
             ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
+
+    # breakdown pass (not the timed region): every call bracketed, and the
+    # dominant kernel picked from it
+    n_prof = max(5, min(args.steps, 20))
+    prof = [(new_events(4), new_events(2)) for _ in range(n_prof)]
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i, (ev, kev) in enumerate(prof):
+        step(args.warmup + i, ev, kev)
+    torch.cuda.synchronize()
+
+    def span(evs, a, b):
+        return np.array([e[a].elapsed_time(e[b]) for e in evs]) * 1e3   # us
+
+    pev, pkev = [p[0] for p in prof], [p[1] for p in prof]
+    append_us, prefill_us, decode_us = span(pev, 0, 1), span(pev, 1, 2), span(pev, 2, 3)
+    stream_us = span(pkev, 0, 1)
+    kernels = {"decode_stream_kernel": float(stream_us.mean()),
+               "reshape_and_cache_kernel": float(append_us.mean())}
+    if pre is not None:
+        kernels["prefill_kernel"] = float(prefill_us.mean())
+    dom = max(kernels, key=kernels.get)
+
+    # timed region: exactly K steps; only the dominant kernel is bracketed
+    tev = [new_events(2) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events[i])
+    for i, e in enumerate(tev):
+        if dom == "decode_stream_kernel":
+            step(i, None, e)
+        elif dom == "prefill_kernel":
+            step(i, (None, e[0], e[1], None))
+        else:
+            step(i, (e[0], e[1], None, None))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    append_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    prefill_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    decode_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    dom_us = span(tev, 0, 1)
     step_ms = wall * 1e3 / args.steps
-    dec_avg = float(decode_ms.mean())
-    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
     value = kv_bytes / (step_ms * 1e-3) / 1e9
 
+    if dom == "prefill_kernel":
+        work = prefill_flops(wl)
+        achieved = work / (float(dom_us.mean()) * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                "traffic": None if read_traffic(dom, args.config) is None else round(read_traffic(dom, args.config)),
+                "work_per_launch": work, "avg_us": round(float(dom_us.mean()), 2)}
+    else:
+        # decode bytes: K and V of every context token read once
+        achieved = kv_bytes / (float(dom_us.mean()) * 1e-6) / 1e9
+        tr = read_traffic(dom, args.config) if dom in KERNEL_SOURCES else None
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if tr is None else round(tr), "work_per_launch": kv_bytes,
+                "avg_us": round(float(dom_us.mean()), 2)}
+
+    def pct(a):
+        return {"avg": round(float(a.mean()), 2), "p10": round(float(np.percentile(a, 10)), 2),
+                "p50": round(float(np.percentile(a, 50)), 2), "p90": round(float(np.percentile(a, 90)), 2)}
+
     res = {
-        "metric": "paged-attn decode us/step + effective KV GB/s (% HBM peak), Llama-3-8B shape",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -176,21 +376,22 @@ def main():
             "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": 16,
             "context_tokens": int(wl.context_lens.sum()), "pool_blocks": wl.num_blocks,
             "seed": seed, "kv_bytes_per_step": kv_bytes, "pool_copies": len(pools),
+            "prefill_rows": None if pre is None else int(wl.prefill.query_start_loc[-1]),
         },
         "timing_us": {
-            "append_avg": round(float(append_ms.mean()) * 1e3, 2),
-            "prefill_avg": round(float(prefill_ms.mean()) * 1e3, 2) if pre is not None else None,
-            "decode_avg": round(dec_avg * 1e3, 2),
-            "decode_p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
-            "decode_p50": round(float(np.percentile(decode_ms, 50)) * 1e3, 2),
-            "decode_p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2),
+            "dominant_kernel_timed": pct(dom_us),
+            "breakdown_steps": n_prof,
+            "append_call": pct(append_us),
+            "prefill_call": pct(prefill_us) if pre is not None else None,
+            "decode_call": pct(decode_us),
+            "decode_stream_kernel": pct(stream_us),
+            "decode_kv_gbs_call": round(kv_bytes / (float(decode_us.mean()) * 1e-6) / 1e9, 2),
         },
-        "roofline": {
-            "kernel": "pa_decode",
-            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        },
+        "roofline": roof,
     }
+    if pre is not None:
+        pf = prefill_flops(wl)
+        res["timing_us"]["prefill_tflops"] = round(pf / (float(prefill_us.mean()) * 1e-6) / 1e12, 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(res), flush=True)

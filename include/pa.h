@@ -118,6 +118,25 @@ int pa_decode(void *out, const void *q,
               int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * pa_decode with the main kernel timed: identical arguments, behaviour and
+ * errors, plus two hipEvent_t handles, created by and owned by the caller
+ * (either may be NULL).  The streaming kernel is launched with
+ * hipExtLaunchKernel, which sets kernel_start to the kernel's start and
+ * kernel_stop to its end, so hipEventElapsedTime(kernel_start, kernel_stop)
+ * is that kernel's duration; the kernel that then merges split contexts is not
+ * included.  For benchmarks and profilers; pa_decode is this call with both
+ * events NULL.
+ */
+int pa_decode_timed(void *out, const void *q,
+                    const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                    void *workspace, size_t workspace_bytes, void *stream,
+                    void *kernel_start, void *kernel_stop);
+
 /* Bytes of workspace pa_prefill_chunk needs (currently always 0). */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows,
                                  int32_t num_q_heads, int32_t head_dim,

@@ -144,6 +144,16 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
               int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, void* workspace,
               size_t workspace_bytes, void* stream) {
+    return pa_decode_timed(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, workspace,
+                           workspace_bytes, stream, nullptr, nullptr);
+}
+
+int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream, void* kernel_start, void* kernel_stop) {
     int rc = check_dtype(dtype);
     if (rc) return rc;
     if (num_seqs < 0) return PA_EINVAL;
@@ -189,7 +199,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.scale_log2 = scale * 1.4426950408889634f;
     // PA_DECODE_STAGES (2, 3 or 4) selects the pipeline depth, for sweeps
     const int stages = env_int("PA_DECODE_STAGES", pa::kDecodeStages);
-    hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, static_cast<hipStream_t>(stream));
+    hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, static_cast<hipStream_t>(stream),
+                                     static_cast<hipEvent_t>(kernel_start), static_cast<hipEvent_t>(kernel_stop));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 

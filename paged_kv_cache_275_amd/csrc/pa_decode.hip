@@ -56,6 +56,8 @@
 //  * Tokens >= n in a sequence's last block are masked (score -inf, V zeroed),
 //    so stale slots -- even NaN -- never reach the result.  Sequences with no
 //    tokens get zero rows.
+#include <hip/hip_ext.h>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -806,21 +808,31 @@ size_t decode_stream_lds_bytes(int num_seqs) {
            (size_t)kDecodeWaves * 4 * 8 * 4 * sizeof(uint32_t);
 }
 
+// Events, when given, take the kernel's own start and stop times from its
+// dispatch (hipExtLaunchKernel): no extra packets on the stream.
 template <typename T, int D, int GP, int STAGES>
-static hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const size_t lds = decode_stream_lds_bytes(a.num_seqs);
-    hipLaunchKernelGGL((decode_stream_kernel<T, D, GP, kDecodeWaves, STAGES, kDecodeWindow>),
-                       dim3((a.waves + kDecodeWaves - 1) / kDecodeWaves), dim3(kDecodeWaves * kWave), lds, stream, a);
+    const dim3 grid((a.waves + kDecodeWaves - 1) / kDecodeWaves), block(kDecodeWaves * kWave);
+    auto kernel = decode_stream_kernel<T, D, GP, kDecodeWaves, STAGES, kDecodeWindow>;
+    if (ev_start || ev_stop) {
+        DecodeArgs arg = a;
+        void* args[] = {&arg};
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, stream, ev_start,
+                                  ev_stop, 0);
+    }
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int D, int GP>
-static hipError_t launch_decode_g(const DecodeArgs& a, int stages, hipStream_t stream) {
+static hipError_t launch_decode_g(const DecodeArgs& a, int stages, hipStream_t stream, hipEvent_t ev_start,
+                                  hipEvent_t ev_stop) {
     hipError_t e;
     switch (stages) {
-        case 2: e = launch_stream<T, D, GP, 2>(a, stream); break;
-        case 3: e = launch_stream<T, D, GP, 3>(a, stream); break;
-        default: e = launch_stream<T, D, GP, 4>(a, stream); break;
+        case 2: e = launch_stream<T, D, GP, 2>(a, stream, ev_start, ev_stop); break;
+        case 3: e = launch_stream<T, D, GP, 3>(a, stream, ev_start, ev_stop); break;
+        default: e = launch_stream<T, D, GP, 4>(a, stream, ev_start, ev_stop); break;
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_fixup_kernel<T, D, GP>), dim3(a.waves), dim3(GP * kWave), 0, stream, a);
@@ -828,23 +840,24 @@ static hipError_t launch_decode_g(const DecodeArgs& a, int stages, hipStream_t s
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int stages, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int stages, hipStream_t stream, hipEvent_t e0,
+                                  hipEvent_t e1) {
     switch (gp) {
-        case 1: return launch_decode_g<T, D, 1>(a, stages, stream);
-        case 2: return launch_decode_g<T, D, 2>(a, stages, stream);
-        case 4: return launch_decode_g<T, D, 4>(a, stages, stream);
-        default: return launch_decode_g<T, D, 8>(a, stages, stream);
+        case 1: return launch_decode_g<T, D, 1>(a, stages, stream, e0, e1);
+        case 2: return launch_decode_g<T, D, 2>(a, stages, stream, e0, e1);
+        case 4: return launch_decode_g<T, D, 4>(a, stages, stream, e0, e1);
+        default: return launch_decode_g<T, D, 8>(a, stages, stream, e0, e1);
     }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages,
-                         hipStream_t stream) {
+                         hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     if (dtype_bf16) {
-        return head_dim == 64 ? launch_decode_d<uint16_t, 64>(a, gp, stages, stream)
-                              : launch_decode_d<uint16_t, 128>(a, gp, stages, stream);
+        return head_dim == 64 ? launch_decode_d<uint16_t, 64>(a, gp, stages, stream, e0, e1)
+                              : launch_decode_d<uint16_t, 128>(a, gp, stages, stream, e0, e1);
     }
-    return head_dim == 64 ? launch_decode_d<float, 64>(a, gp, stages, stream)
-                          : launch_decode_d<float, 128>(a, gp, stages, stream);
+    return head_dim == 64 ? launch_decode_d<float, 64>(a, gp, stages, stream, e0, e1)
+                          : launch_decode_d<float, 128>(a, gp, stages, stream, e0, e1);
 }
 
 }  // namespace pa

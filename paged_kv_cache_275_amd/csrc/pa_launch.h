@@ -81,8 +81,10 @@ struct PrefillArgs {
 constexpr int kPrefillMaxGroup = 16;
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, hipStream_t stream);
+// Launches the streaming kernel and the split-segment merge.  Non-null events
+// receive the streaming kernel's start and stop times.
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int num_tokens, int row_bytes,

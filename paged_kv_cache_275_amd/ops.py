@@ -48,6 +48,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
                               ctypes.c_int, p, sz, p]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_timed.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
+                                    ctypes.c_int, p, sz, p, p, p]
+    lib.pa_decode_timed.restype = ctypes.c_int
     lib.pa_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_prefill_workspace_size.restype = sz
     lib.pa_prefill_chunk.argtypes = [p, p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32, i64,
@@ -99,10 +102,8 @@ def _stream_handle(t, stream) -> int:
     return s.cuda_stream
 
 
-def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
-    """k_cache[slot // 16, slot % 16] = key[i] (and value), for slot_mapping[i] >= 0."""
+def _reshape_and_cache_args(key, value, k_cache, v_cache, slot_mapping, stream) -> tuple:
     import torch
-    lib = load_library()
     _need(key, "key", dim=3)
     _need(value, "value", key.dtype, 3)
     _need(k_cache, "k_cache", key.dtype, 4)
@@ -113,10 +114,31 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -
         raise ValueError("key/value [T, Hkv, D] must match caches [NB, 16, Hkv, D]")
     if slot_mapping.shape[0] != key.shape[0]:
         raise ValueError("slot_mapping must have one entry per token")
-    rc = lib.pa_reshape_and_cache(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
-                                  v_cache.data_ptr(), slot_mapping.data_ptr(), key.shape[0], hkv,
-                                  d, bs, nb, _dtype_code(key), _stream_handle(key, stream))
-    _check(lib, "pa_reshape_and_cache", rc)
+    return (key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            slot_mapping.data_ptr(), key.shape[0], hkv, d, bs, nb, _dtype_code(key),
+            _stream_handle(key, stream))
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """k_cache[slot // 16, slot % 16] = key[i] (and value), for slot_mapping[i] >= 0."""
+    lib = load_library()
+    args = _reshape_and_cache_args(key, value, k_cache, v_cache, slot_mapping, stream)
+    _check(lib, "pa_reshape_and_cache", lib.pa_reshape_and_cache(*args))
+
+
+def bind_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """Check the arguments once; return f() that enqueues the same append again.
+
+    For loops that repeat one call on fixed buffers (benchmarks): the returned
+    function only crosses the C ABI.  The tensors must stay alive.
+    """
+    lib = load_library()
+    args = _reshape_and_cache_args(key, value, k_cache, v_cache, slot_mapping, stream)
+    fn = lib.pa_reshape_and_cache
+
+    def call():
+        _check(lib, "pa_reshape_and_cache", fn(*args))
+    return call
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
@@ -133,11 +155,8 @@ def decode_workspace(q, k_cache, block_tables):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
 
 
-def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace=None,
-           stream=None) -> None:
-    """Paged-attention decode into out [S, Hq, D]."""
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace, stream) -> tuple:
     import torch
-    lib = load_library()
     _need(q, "q", dim=3)
     _need(out, "out", q.dtype, 3)
     _need(k_cache, "k_cache", q.dtype, 4)
@@ -152,11 +171,50 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, w
         raise ValueError("block_tables and context_lens need one row per sequence")
     if workspace is None:
         workspace = decode_workspace(q, k_cache, block_tables)
-    rc = lib.pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                       block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), s,
-                       hq, hkv, d, bs, nb, float(scale), _dtype_code(q), workspace.data_ptr(),
-                       workspace.numel() * workspace.element_size(), _stream_handle(q, stream))
-    _check(lib, "pa_decode", rc)
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), s,
+            hq, hkv, d, bs, nb, float(scale), _dtype_code(q), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(q, stream))
+    return args, workspace
+
+
+def _event_handles(kernel_events):
+    ev0, ev1 = kernel_events
+    if not ev0.cuda_event or not ev1.cuda_event:
+        raise ValueError("kernel_events must be created (recorded once) before use")
+    return ev0.cuda_event, ev1.cuda_event
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace=None,
+           stream=None, kernel_events=None) -> None:
+    """Paged-attention decode into out [S, Hq, D].
+
+    kernel_events: optional (start, stop) pair of torch.cuda.Event, already
+    created (recorded once); they receive the start and stop times of the
+    library's streaming kernel (pa_decode_timed).
+    """
+    lib = load_library()
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace, stream)
+    if kernel_events is None:
+        _check(lib, "pa_decode", lib.pa_decode(*args))
+    else:
+        _check(lib, "pa_decode_timed", lib.pa_decode_timed(*args, *_event_handles(kernel_events)))
+
+
+def bind_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace=None,
+                stream=None):
+    """Check the arguments once; return f(kernel_events=None) that enqueues the
+    same decode again (see bind_reshape_and_cache)."""
+    lib = load_library()
+    args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace, stream)
+    plain, timed = lib.pa_decode, lib.pa_decode_timed
+
+    def call(kernel_events=None, _keep=ws):
+        if kernel_events is None:
+            _check(lib, "pa_decode", plain(*args))
+        else:
+            _check(lib, "pa_decode_timed", timed(*args, *kernel_events))
+    return call
 
 
 def prefill_workspace_size(num_seqs, total_query_rows, num_q_heads, head_dim, max_blocks_per_seq,
@@ -165,11 +223,9 @@ def prefill_workspace_size(num_seqs, total_query_rows, num_q_heads, head_dim, ma
                                                         head_dim, max_blocks_per_seq, block_size))
 
 
-def prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
-                  scale: float, workspace=None, stream=None) -> None:
-    """Causal chunked prefill into out [rows, Hq, D] (see pa_prefill_chunk)."""
+def _prefill_args(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale, workspace,
+                  stream) -> tuple:
     import torch
-    lib = load_library()
     _need(q, "q", dim=3)
     _need(out, "out", q.dtype, 3)
     _need(k_cache, "k_cache", q.dtype, 4)
@@ -189,9 +245,31 @@ def prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, conte
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.pa_prefill_chunk(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                              block_tables.data_ptr(), block_tables.shape[1],
-                              query_start_loc.data_ptr(), rows, context_lens.data_ptr(), sp, hq,
-                              hkv, d, bs, nb, float(scale), _dtype_code(q), ws_ptr, ws_bytes,
-                              _stream_handle(q, stream))
-    _check(lib, "pa_prefill_chunk", rc)
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), block_tables.shape[1], query_start_loc.data_ptr(), rows,
+            context_lens.data_ptr(), sp, hq, hkv, d, bs, nb, float(scale), _dtype_code(q), ws_ptr,
+            ws_bytes, _stream_handle(q, stream))
+    return args, workspace
+
+
+def prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                  scale: float, workspace=None, stream=None) -> None:
+    """Causal chunked prefill into out [rows, Hq, D] (see pa_prefill_chunk)."""
+    lib = load_library()
+    args, _ = _prefill_args(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale,
+                            workspace, stream)
+    _check(lib, "pa_prefill_chunk", lib.pa_prefill_chunk(*args))
+
+
+def bind_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                       scale: float, workspace=None, stream=None):
+    """Check the arguments once; return f() that enqueues the same prefill again
+    (see bind_reshape_and_cache)."""
+    lib = load_library()
+    args, ws = _prefill_args(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale,
+                             workspace, stream)
+    fn = lib.pa_prefill_chunk
+
+    def call(_keep=ws):
+        _check(lib, "pa_prefill_chunk", fn(*args))
+    return call

@@ -25,7 +25,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = ops.header_functions()
     assert {"pa_reshape_and_cache", "pa_decode", "pa_prefill_chunk", "pa_decode_workspace_size",
-            "pa_prefill_workspace_size", "pa_status_string"} <= set(names)
+            "pa_prefill_workspace_size", "pa_status_string", "pa_decode_timed"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libpa.so does not export {n}"
     out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
@@ -40,13 +40,17 @@ def test_status_strings(lib):
     assert lib.pa_status_string(123) == b"unknown pa_status"
 
 
-def _decode(lib, **kw):
+def _decode(lib, timed=False, **kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=4, cl=FAKE, s=2, hq=8, hkv=2, d=128,
              bs=16, nb=64, scale=0.1, dtype=ops.PA_BF16, ws=FAKE, ws_bytes=1 << 30, stream=None)
     a.update(kw)
-    return lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["s"],
-                         a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
-                         a["ws"], a["ws_bytes"], a["stream"])
+    args = (a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["s"],
+            a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+            a["ws"], a["ws_bytes"], a["stream"])
+    if timed:
+        # fake event handles: argument checks come first, so they are never used
+        return lib.pa_decode_timed(*args, FAKE, FAKE)
+    return lib.pa_decode(*args)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -69,6 +73,7 @@ def _decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
+    assert _decode(lib, timed=True, **kw) == code
 
 
 def test_decode_empty_batch_is_noop(lib):
