@@ -65,6 +65,19 @@ namespace pa {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: lazy max, exp2 <= 256
 
+// Finished segments are staged in LDS and written out once the wave's loads are
+// done (see the kernel).  A slot holds one segment: a header of 4 words, two
+// floats per head, and the wave's reduced sums (GP*D floats).  Slots per wave:
+// about 8 KB of LDS, at least 2.
+template <int GP, int D>
+struct StageGeom {
+    static constexpr int kMeta = 4 + 2 * GP;
+    static constexpr int kVals = GP * D;
+    static constexpr int kWords = kMeta + kVals;
+    static constexpr int kSlots = (2048 / kVals) > 2 ? (2048 / kVals) : 2;
+    static constexpr size_t kBytesPerWave = (size_t)kSlots * kWords * sizeof(float);
+};
+
 template <typename T, int D>
 struct DecodeGeom {
     static constexpr int kElem = sizeof(T);
@@ -395,8 +408,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * NW + threadIdx.x / kWave);
     if (wv >= a.waves) return;  // padding waves of the last workgroup (no barrier follows)
     const int lane = threadIdx.x & (kWave - 1);
-    // no split segment starts in this wave unless noted below
-    if (lane == 0) a.ws_split[wv].seq = -1;
     const int kvg = wv % n_kvg;                  // this wave's head group
     const long long grp = wv / n_kvg;            // its wave group
     const int hk = kvg / a.groups_per_kv;        // kv head
@@ -409,6 +420,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         // an empty range (a share smaller than a unit): a zero-weight record in
         // slot 0, in case the wave lies inside a split segment's span of waves
         if (lane < GP) *reinterpret_cast<float2*>(a.ws_ml + ((size_t)wv * 2 * GP + lane) * 2) = make_float2(-INFINITY, 0.f);
+        if (lane == 0) a.ws_split[wv].seq = -1;  // no split segment starts here
         return;  // wave-uniform; no barrier follows
     }
 
@@ -437,6 +449,51 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     const int mtok = lane & 15;
     const uint32_t kmf_off = ((uint32_t)mtok * hkv_heads) * D + 8 * mrow;
     uint32_t* lp = reinterpret_cast<uint32_t*>(tabs + NW * WIN) + (wv % NW) * (4 * 8 * 4);
+
+    // Staging of finished segments.  A global store holds up the completion
+    // count of every load issued after it until the store itself completes,
+    // which under a full read stream takes about as long as a load: a store in
+    // mid-stream stalls the ring.  So finished segments wait in LDS and are
+    // written after the wave's last load (or when the slots run out).
+    using SG = StageGeom<GP, D>;
+    constexpr int kCh = GP * kDpl / 8;  // reduced sums per lane
+    float* stage = reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(tabs + NW * WIN) + NW * (4 * 8 * 4)) +
+                   (wv % NW) * SG::kSlots * SG::kWords;
+    int nstaged = 0;
+    const int gl = (tg * kCh) / kDpl;  // head of this lane's reduced sums
+    const int d0 = (tg * kCh) % kDpl;  // their first element among the lane's dims
+    SplitNote note;                    // written at the end
+    note.seq = -1;
+    note.kvg = kvg;
+    note.last_wave = 0;
+    note.first_slot = 0;
+
+    auto flush = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int j = 0; j < nstaged; ++j) {
+            const float* sl = stage + j * SG::kWords;
+            const int kind = __builtin_amdgcn_readfirstlane(__float_as_int(sl[0]));
+            const int base = __builtin_amdgcn_readfirstlane(__float_as_int(sl[1]));
+            float v[kCh];
+#pragma unroll
+            for (int i = 0; i < kCh; ++i) v[i] = sl[SG::kMeta + i * kWave + lane];
+            const float x = sl[4 + gl], y = sl[4 + GP + gl];
+            if (gl < nvh) {
+                if (kind == 0) {
+                    store_run<T, kE, kCh>(reinterpret_cast<T*>(a.out) + (size_t)(base + gl) * D, v, x, d0, dl);
+                } else {
+                    store_run<float, kE, kCh>(a.ws_acc + (size_t)(base + gl) * D, v, 1.f, d0, dl);
+                    if (dl == 0 && d0 == 0) *reinterpret_cast<float2*>(a.ws_ml + (size_t)(base + gl) * 2) = make_float2(x, y);
+                }
+            }
+        }
+        nstaged = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
 
     uint32_t qb[GP][kQb], qnb[GP][kQb];
     float qf[GP][kDpl], qnf[GP][kDpl];
@@ -493,37 +550,30 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         }
     };
 
-    // Segment (cs, kvg) is done: write its rows, or leave a partial record.
-    // The partial sums are reduce-scattered over the token groups, so lane
-    // (tg, dl) ends with kCh complete sums of one head: elements d0 .. d0+kCh-1
-    // of its dims of head gl.
+    // Segment (cs, kvg) is done: stage its rows, or a partial record.  The
+    // partial sums are reduce-scattered over the token groups, so lane (tg, dl)
+    // ends with kCh complete sums of head gl: elements d0 .. d0+kCh-1 of its dims.
     auto finish_segment = [&]() {
-        constexpr int kCh = GP * kDpl / 8;
         const bool complete = seg_first_blk == 0 && cblk == cnb - 1;
         const int slot = first_seg ? 0 : 1;
         float red[kCh];
         reduce_scatter8<GP, kDpl>(red, acc, lane);
-        const int gl = (tg * kCh) / kDpl;
-        const int d0 = (tg * kCh) % kDpl;
-        float mg = m[0], lg = sum_groups8(l[0]);
+        float* sl = stage + nstaged * SG::kWords;
 #pragma unroll
-        for (int g = 1; g < GP; ++g) {
-            const float lt = sum_groups8(l[g]);
-            if (gl == g) {
-                mg = m[g];
-                lg = lt;
+        for (int i = 0; i < kCh; ++i) sl[SG::kMeta + i * kWave + lane] = red[i];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            const float lt = sum_groups8(l[g]);  // the same on every lane
+            if (lane == 0) {
+                sl[4 + g] = complete ? 1.f / lt : m[g];
+                sl[4 + GP + g] = lt;
             }
         }
-        if (gi0 + gl < a.group) {
-            if (complete) {
-                T* orow = reinterpret_cast<T*>(a.out) + ((size_t)cs * a.num_q_heads + h0 + gl) * D;
-                store_run<T, kE, kCh>(orow, red, 1.f / lg, d0, dl);
-            } else {
-                const size_t rec = ((size_t)wv * 2 + slot) * GP + gl;
-                store_run<float, kE, kCh>(a.ws_acc + rec * D, red, 1.f, d0, dl);
-                if (dl == 0 && d0 == 0) *reinterpret_cast<float2*>(a.ws_ml + rec * 2) = make_float2(mg, lg);
-            }
+        if (lane == 0) {
+            sl[0] = __int_as_float(complete ? 0 : 1);
+            sl[1] = __int_as_float(complete ? cs * a.num_q_heads + h0 : (wv * 2 + slot) * GP);
         }
+        ++nstaged;
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
             m[g] = -INFINITY;
@@ -533,19 +583,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
-        if (!complete && seg_first_blk == 0 && lane == 0) {
+        if (!complete && seg_first_blk == 0) {
             // this wave holds the segment's first unit: note it for the fix-up,
             // with the wave (same head group) whose group holds the first tick
             // of the segment's last block
             const long long t_last = (long long)tpref[cs] + (long long)(cnb - 1) * R;
-            SplitNote sn;
-            sn.seq = cs;
-            sn.kvg = kvg;
-            sn.last_wave = (int)(((t_last + 1) * NG - 1) / TT) * n_kvg + kvg;
-            sn.first_slot = first_seg ? 0 : 1;
-            a.ws_split[wv] = sn;
+            note.seq = cs;
+            note.last_wave = (int)(((t_last + 1) * NG - 1) / TT) * n_kvg + kvg;
+            note.first_slot = slot;
         }
         first_seg = false;
+        if (nstaged == SG::kSlots) flush();  // rare: many short sequences in one range
     };
 
     for (int wb0 = u_begin; wb0 < u_end; wb0 += WIN) {
@@ -722,6 +770,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             }
         }
     }
+    flush();
+    if (lane == 0) a.ws_split[wv] = note;
 }
 
 // Merge the partial records of the split segment noted by wave w (if any):
@@ -802,17 +852,19 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
 }
 
 // ---------------------------------------------------------------- launchers
-size_t decode_stream_lds_bytes(int num_seqs) {
+template <int GP, int D>
+static size_t decode_stream_lds_bytes(int num_seqs) {
     return 2 * (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int) +
            (size_t)kDecodeWaves * kDecodeWindow * sizeof(uint4) +
-           (size_t)kDecodeWaves * 4 * 8 * 4 * sizeof(uint32_t);
+           (size_t)kDecodeWaves * 4 * 8 * 4 * sizeof(uint32_t) +
+           (size_t)kDecodeWaves * StageGeom<GP, D>::kBytesPerWave;
 }
 
 // Events, when given, take the kernel's own start and stop times from its
 // dispatch (hipExtLaunchKernel): no extra packets on the stream.
 template <typename T, int D, int GP, int STAGES>
 static hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
-    const size_t lds = decode_stream_lds_bytes(a.num_seqs);
+    const size_t lds = decode_stream_lds_bytes<GP, D>(a.num_seqs);
     const dim3 grid((a.waves + kDecodeWaves - 1) / kDecodeWaves), block(kDecodeWaves * kWave);
     auto kernel = decode_stream_kernel<T, D, GP, kDecodeWaves, STAGES, kDecodeWindow>;
     if (ev_start || ev_stop) {

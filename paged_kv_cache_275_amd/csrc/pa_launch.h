@@ -59,8 +59,6 @@ struct DecodeArgs {
     float scale_log2;   // scale * log2(e)
 };
 
-size_t decode_stream_lds_bytes(int num_seqs);
-
 struct PrefillArgs {
     void* out;
     const void* q;

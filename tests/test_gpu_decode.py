@@ -116,36 +116,72 @@ def test_zero_length_context_gives_zeros():
     assert_attention_close(got, ref, wl.dtype, "zero-length")
 
 
+def _bf16_bits(rng, shape):
+    return (rng.standard_normal(shape).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _random_bf16_case(rng, hq, hkv, d, lens, spare_blocks=4):
+    """A bf16 pool holding len(lens) sequences in shuffled blocks (NaN elsewhere)."""
+    s = len(lens)
+    need = [-(-int(n) // 16) for n in lens]
+    nb = sum(need) + spare_blocks
+    mb = max(1, max(need))
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((s, mb), -1, np.int32)
+    off = 0
+    for i, k in enumerate(need):
+        bt[i, :k] = perm[off:off + k]
+        off += k
+    kc = np.full((nb, 16, hkv, d), 0x7FC0, np.uint16)
+    vc = kc.copy()
+    tok = np.concatenate([np.arange(int(n)) for n in lens]) if sum(lens) else np.zeros(0, np.int64)
+    seq = np.repeat(np.arange(s), lens)
+    slot = bt[seq, tok // 16].astype(np.int64) * 16 + tok % 16
+    kc.reshape(-1, hkv, d)[slot] = _bf16_bits(rng, (len(slot), hkv, d))
+    vc.reshape(-1, hkv, d)[slot] = _bf16_bits(rng, (len(slot), hkv, d))
+    q = _bf16_bits(rng, (s, hq, d))
+    return q, kc, vc, bt, np.asarray(lens, np.int32)
+
+
+def _decode_bf16(q, kc, vc, bt, lens, scale):
+    from tests._gpu import to_dev
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.decode(out, to_dev(q), to_dev(kc), to_dev(vc), to_dev(bt), to_dev(lens), scale)
+    torch.cuda.synchronize()
+    return widen_dev(out)
+
+
 def test_group_sizes_and_head_dims():
     """GQA groups 1, 2, 3, 8, 16 and head_dim 64 on a reshaped small workload."""
     for hq, hkv, d in [(8, 8, 128), (6, 2, 64), (24, 3, 128), (16, 2, 64), (32, 2, 128)]:
         rng = np.random.default_rng(hq * 1000 + hkv)
-        s, nb = 3, 64
-        lens = np.array([1, 37, 300], np.int32)
-        mb = 20
-        perm = rng.permutation(nb).astype(np.int32)
-        bt = np.full((s, mb), -1, np.int32)
-        off = 0
-        for i, n in enumerate(lens):
-            k = -(-int(n) // 16)
-            bt[i, :k] = perm[off:off + k]
-            off += k
-        kc = np.full((nb, 16, hkv, d), 0x7FC0, np.uint16)
-        vc = kc.copy()
-        for i, n in enumerate(lens):
-            t = np.arange(int(n))
-            slot = bt[i, t // 16].astype(np.int64) * 16 + t % 16
-            kc.reshape(-1, hkv, d)[slot] = (rng.standard_normal((len(t), hkv, d)).astype(np.float32)
-                                            .view(np.uint32) >> 16).astype(np.uint16)
-            vc.reshape(-1, hkv, d)[slot] = (rng.standard_normal((len(t), hkv, d)).astype(np.float32)
-                                            .view(np.uint32) >> 16).astype(np.uint16)
-        q = (rng.standard_normal((s, hq, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
-        from tests._gpu import to_dev
-        out = torch.empty((s, hq, d), dtype=torch.bfloat16, device="cuda")
-        ops.decode(out, to_dev(q), to_dev(kc), to_dev(vc), to_dev(bt), to_dev(lens), 0.09)
-        torch.cuda.synchronize()
+        q, kc, vc, bt, lens = _random_bf16_case(rng, hq, hkv, d, [1, 37, 300], spare_blocks=40)
+        got = _decode_bf16(q, kc, vc, bt, lens, 0.09)
         ref = oracle.decode(q, kc, vc, bt, lens, 0.09)
-        assert_attention_close(widen_dev(out), ref, "bf16", f"hq{hq}/hkv{hkv}/d{d}")
+        assert_attention_close(got, ref, "bf16", f"hq{hq}/hkv{hkv}/d{d}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (32, 4, 128)])
+def test_decode_max_sequences(hq, hkv, d):
+    """8192 sequences (the most one call takes) of 0..40 tokens: every wave
+    closes many segments, more than it can stage at once."""
+    rng = np.random.default_rng(8192 + hq)
+    lens = rng.integers(0, 41, 8192)
+    lens[rng.random(8192) < 0.05] = 0
+    print(f"[gpu] max sequences hq={hq} hkv={hkv} d={d} sumN={int(lens.sum())}", flush=True)
+    q, kc, vc, bt, lens = _random_bf16_case(rng, hq, hkv, d, lens.tolist())
+    got = _decode_bf16(q, kc, vc, bt, lens, 1.0 / np.sqrt(d))
+    ref = oracle.decode(q, kc, vc, bt, lens, 1.0 / np.sqrt(d))
+    assert np.all(got[lens == 0] == 0.0)
+    assert_attention_close(got, ref, "bf16", f"S=8192 hq{hq}/hkv{hkv}/d{d}")
+
+
+@pytest.mark.parametrize("ticks", ["0", "1", "64"])
+def test_decode_switch_cost_does_not_change_results(ticks, monkeypatch):
+    """The segment cost only moves the split points between wave groups."""
+    monkeypatch.setenv("PA_DECODE_SWITCH_TICKS", ticks)
+    wl = W.make_workload("llama3_8b", seed=31, num_seqs=40)
+    _check_workload(wl, f"switch_ticks={ticks}")
 
 
 def test_invalid_arguments_raise():
