@@ -15,10 +15,17 @@
 //    its COLS = RT * GP columns are (query row, head) pairs, all heads of the
 //    GQA group side by side, so every K/V tile staged in LDS serves the whole
 //    group.  Wave w owns CT tiles of 16 columns.
+//  * Work items (sequence, kv head, row tile) are numbered so that the items
+//    of one (sequence, kv head) are consecutive, latest rows (the most keys)
+//    first, and the grid is remapped so that each XCD (workgroup id mod 8)
+//    takes one contiguous eighth of the items: the workgroups that read the
+//    same K/V share one L2, and each XCD starts on its longest items.
 //  * Keys stream through LDS in tiles of 64 (four 16-token blocks, resolved
 //    through the block table).  K is stored row-major; V is stored transposed
-//    (V^T[dim][key]) so that it can be an MFMA A operand.  The next tile's
-//    global loads are issued before the current tile is computed.
+//    (V^T[dim][key]) so that it can be an MFMA A operand.  Global loads run two
+//    tiles ahead in registers, always issued (block index clamped into the
+//    sequence, keys past the context masked afterwards), so the load counter
+//    never has to drain and no load waits on another.
 //  * Scores are computed transposed, S^T = K Q^T: lane l then holds column l%16
 //    and keys 4*(l/16) .. +3 of each 16-key subtile.  Row maxima and sums are
 //    per-lane work plus two lane swaps, and the probabilities of two subtiles
@@ -31,6 +38,8 @@
 #include "pa_launch.h"
 
 namespace pa {
+
+constexpr float kSlack = 8.0f;  // log2 units: lazy running max, exp2 <= 256
 
 template <int D, int GP, int NW, int CT>
 __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
@@ -50,23 +59,34 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
     __shared__ __align__(16) uint16_t k_lds[kKT * kKP];
     __shared__ __align__(16) uint16_t vt_lds[D * kVP];
 
-    const int hk = blockIdx.y;
-    // ---- which sequence and row tile: flat enumeration over sequences
-    int s = 0, tile = blockIdx.x, r0 = 0, c = 0;
-    for (; s < a.num_seqs; ++s) {
+    // ---- work item: see the header
+    const int S = a.num_seqs;
+    const int hkv_heads = a.num_kv_heads;
+    int total = 0;
+    for (int q = 0; q < S; ++q) {
+        const int cq = a.query_start_loc[q + 1] - a.query_start_loc[q];
+        total += (cq + kRT - 1) / kRT * hkv_heads;
+    }
+    const int per_xcd = (total + 7) / 8;
+    const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if ((int)(blockIdx.x / 8) >= per_xcd || item >= total) return;  // uniform: grid is an upper bound
+    int s = 0, base = 0, r0 = 0, c = 0, tiles = 0;
+    for (; s < S; ++s) {
         r0 = a.query_start_loc[s];
         c = a.query_start_loc[s + 1] - r0;
-        const int nt = (c + kRT - 1) / kRT;
-        if (tile < nt) break;
-        tile -= nt;
+        tiles = (c + kRT - 1) / kRT;
+        if (item < base + tiles * hkv_heads) break;
+        base += tiles * hkv_heads;
     }
-    if (s >= a.num_seqs) return;  // uniform: grid is an upper bound
+    const int hk = (item - base) / tiles;
+    const int tile = tiles - 1 - (item - base) % tiles;  // latest rows first
     const int n = a.context_lens[s];
     const int i0 = tile * kRT;
     const int rows = min(kRT, c - i0);
     const int pos0 = n - c + i0;           // position of the workgroup's first row
     const int pmax = pos0 + rows - 1;      // last key any row needs
     const int ntiles = pmax / kKT + 1;
+    const int nblk = (n + kBlockTokens - 1) / kBlockTokens;  // table entries that may be read
     const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks_per_seq;
 
     const int tid = threadIdx.x;
@@ -74,7 +94,6 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lg = lane >> 4;    // lane group: k-slots 8*lg .. +8, output rows 4*lg .. +3
     const int lc = lane & 15;    // column within a 16-column tile
-    const int hkv_heads = a.num_kv_heads;
     const uint16_t* kcache = reinterpret_cast<const uint16_t*>(a.k_cache);
     const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache);
 
@@ -109,50 +128,70 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
         for (int dt = 0; dt < kDt; ++dt) o[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- staging: K chunks (key, 16-byte chunk) and one 4-key x 8-dim V block
-    uint4 kreg[kKChunks], vreg[4];
+    // ---- staging: K chunks (key, 16-byte chunk) and one 4-key x 8-dim V block,
+    // two tiles in flight
+    // native vector registers (a struct copy would be lowered through memory)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 kreg[2][kKChunks], vreg[2][4];
     const int v_kg = tid / (D / 8);   // keys 4*v_kg .. +3 of the tile
     const int v_dc = tid % (D / 8);   // dims 8*v_dc .. +7
-    auto load_tile = [&](int t) {
+    // the four blocks of tile t (the same for the whole workgroup); entries past
+    // the context are never read: the index is clamped, and the keys such a
+    // block would hold are masked
+    auto tile_blocks = [&](int t) __attribute__((always_inline)) {
+        int4 b;
+        b.x = bt[min(t * 4 + 0, nblk - 1)];
+        b.y = bt[min(t * 4 + 1, nblk - 1)];
+        b.z = bt[min(t * 4 + 2, nblk - 1)];
+        b.w = bt[min(t * 4 + 3, nblk - 1)];
+        return b;
+    };
+    static_assert(kKT == 4 * kBlockTokens, "a key tile is four blocks");
+    auto load_tile = [&](int t, int buf, int4 bq) __attribute__((always_inline)) {
         const int t0 = t * kKT;
+        const int b4[4] = {bq.x, bq.y, bq.z, bq.w};
+        auto blk = [&](int key) {  // block of tile key 0..63, without dynamic indexing
+            const int j = key / kBlockTokens;
+            return j == 0 ? b4[0] : j == 1 ? b4[1] : j == 2 ? b4[2] : b4[3];
+        };
 #pragma unroll
         for (int j = 0; j < kKChunks; ++j) {
             const int q = tid + j * kNT;
             const int key = q / (D / 8);
             const int ch = q % (D / 8);
-            const int tok = t0 + key;
-            if (tok < n) {
-                const int b = bt[tok / kBlockTokens];
-                kreg[j] = *reinterpret_cast<const uint4*>(
-                    kcache + (((size_t)b * kBlockTokens + tok % kBlockTokens) * hkv_heads + hk) * D + ch * 8);
-            } else {
-                kreg[j] = make_uint4(0, 0, 0, 0);
-            }
+            kreg[buf][j] = *reinterpret_cast<const u32x4*>(
+                kcache + (((size_t)blk(key) * kBlockTokens + (t0 + key) % kBlockTokens) * hkv_heads + hk) * D + ch * 8);
         }
+        const int vk = tid < kVBlocks ? 4 * v_kg : 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int tok = t0 + 4 * v_kg + e;
-            if (tid < kVBlocks && tok < n) {
-                const int b = bt[tok / kBlockTokens];
-                vreg[e] = *reinterpret_cast<const uint4*>(
-                    vcache + (((size_t)b * kBlockTokens + tok % kBlockTokens) * hkv_heads + hk) * D + v_dc * 8);
-            } else {
-                vreg[e] = make_uint4(0, 0, 0, 0);
-            }
+            vreg[buf][e] = *reinterpret_cast<const u32x4*>(
+                vcache + (((size_t)blk(vk + e) * kBlockTokens + (t0 + vk + e) % kBlockTokens) * hkv_heads + hk) * D +
+                v_dc * 8);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kKChunks; ++j) {
             const int q = tid + j * kNT;
-            *reinterpret_cast<uint4*>(&k_lds[(q / (D / 8)) * kKP + (q % (D / 8)) * 8]) = kreg[j];
+            *reinterpret_cast<u32x4*>(&k_lds[(q / (D / 8)) * kKP + (q % (D / 8)) * 8]) = kreg[buf][j];
         }
         if (tid >= kVBlocks) return;
+        // keys past the context: V is zero (the slots may hold anything)
+        u32x4 vv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = t * kKT + 4 * v_kg + e < n ? vreg[buf][e] : u32x4{0u, 0u, 0u, 0u};
+        // V^T column of this thread's 4 keys: within each group of 32 keys the
+        // 4-key chunks are stored in the order 0,4,1,5,2,6,3,7, so that the
+        // keys lane group g needs for a 32-key MFMA step (chunks g and g+4)
+        // are 16 contiguous bytes
+        const int xk = v_kg % 8;
+        const int vcol = (v_kg / 8) * 32 + 4 * (xk < 4 ? 2 * xk : 2 * (xk - 4) + 1);
         // transpose the 4 keys x 8 dims block: dim e gets (k0, k1, k2, k3)
-        const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-        const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-        const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-        const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+        const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
+        const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+        const uint32_t w2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
+        const uint32_t w3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // even dim 2j: low halves; odd dim 2j+1: high halves
@@ -160,18 +199,24 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
                                         __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u));
             const uint2 od = make_uint2(__builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u),
                                         __builtin_amdgcn_perm(w3[j], w2[j], 0x07060302u));
-            *reinterpret_cast<uint2*>(&vt_lds[(v_dc * 8 + 2 * j) * kVP + 4 * v_kg]) = ev;
-            *reinterpret_cast<uint2*>(&vt_lds[(v_dc * 8 + 2 * j + 1) * kVP + 4 * v_kg]) = od;
+            *reinterpret_cast<uint2*>(&vt_lds[(v_dc * 8 + 2 * j) * kVP + vcol]) = ev;
+            *reinterpret_cast<uint2*>(&vt_lds[(v_dc * 8 + 2 * j + 1) * kVP + vcol]) = od;
         }
     };
 
-    load_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
+    // Tile t uses register buffer t % 2.  The step is called with a literal
+    // buffer index (the loop runs over pairs of tiles) so that the buffers stay
+    // in registers.
+    auto step = [&](const int t, const int buf, int4& bn) __attribute__((always_inline)) {
         __syncthreads();  // the previous tile is no longer being read
-        store_tile();
+        store_tile(t, buf);
         __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1);
+        load_tile(min(t + 2, ntiles - 1), buf, bn);  // past the end: a repeat, never stored
+        bn = tile_blocks(min(t + 3, ntiles - 1));     // requested a step before it is needed
         const int t0 = t * kKT;
+        // every key of this tile is visible to every row of the workgroup
+        // unless the tile reaches past the first row's position
+        const bool masked = t0 + kKT - 1 > pos0;
 
         // ---- S^T = K Q^T for the four 16-key subtiles
         f32x4_t sacc[4][CT];
@@ -197,34 +242,41 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = t0 + sb * 16 + 4 * lg + r;
-                    const float x = key <= col_pos[ct] ? sacc[sb][ct][r] * a.scale_log2 : -INFINITY;
-                    sv[sb][r] = x;
-                    tmax = fmaxf(tmax, x);
+                    const float x = sacc[sb][ct][r] * a.scale_log2;
+                    sv[sb][r] = !masked || key <= col_pos[ct] ? x : -INFINITY;
+                    tmax = fmaxf(tmax, sv[sb][r]);
                 }
             }
-            // the column's keys live in lanes lc, lc+16, lc+32, lc+48
-            {
+            // Lazy running max: raised only when a score exceeds it by more than
+            // kSlack (log2 units), so exp2 stays <= 2^kSlack and the rescale of
+            // the accumulators is rare.  Tile 0 holds key 0, visible to every
+            // row, so the max is finite from then on.
+            const bool need = tmax > mrun[ct] + kSlack;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                // the column's keys live in lanes lc, lc+16, lc+32, lc+48
                 auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-                auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+                float cm = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+                auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
+                cm = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+                const float mn = fmaxf(mrun[ct], cm);
+                const float alpha = mrun[ct] == -INFINITY ? 0.f : fast_exp2(mrun[ct] - mn);
+                mrun[ct] = mn;
+                lrun[ct] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < kDt; ++dt) o[ct][dt] *= alpha;
             }
-            const float mn = fmaxf(mrun[ct], tmax);
-            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(mrun[ct] - mn);
-            mrun[ct] = mn;
+            const float mc = mrun[ct];
             float psum = 0.f;
             float pv[4][4];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    pv[sb][r] = mn == -INFINITY ? 0.f : fast_exp2(sv[sb][r] - mn);
+                    pv[sb][r] = fast_exp2(sv[sb][r] - mc);
                     psum += pv[sb][r];
                 }
             }
-            lrun[ct] = lrun[ct] * alpha + psum;
-#pragma unroll
-            for (int dt = 0; dt < kDt; ++dt) o[ct][dt] *= alpha;
+            lrun[ct] += psum;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 pb[ct][kk] = make_uint4(pack_bf16x2(pv[2 * kk][0], pv[2 * kk][1]),
@@ -238,14 +290,18 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int dt = 0; dt < kDt; ++dt) {
-                const uint16_t* vrow = &vt_lds[(dt * 16 + lc) * kVP + 32 * kk + 4 * lg];
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-                const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                const uint4 va = *reinterpret_cast<const uint4*>(&vt_lds[(dt * 16 + lc) * kVP + 32 * kk + 8 * lg]);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) o[ct][dt] = mfma16x16x32_bf16(va, pb[ct][kk], o[ct][dt]);
             }
         }
+    };
+    load_tile(0, 0, tile_blocks(0));
+    load_tile(ntiles > 1 ? 1 : 0, 1, tile_blocks(ntiles > 1 ? 1 : 0));  // always issued
+    int4 bnext = tile_blocks(min(2, ntiles - 1));  // blocks of the next tile to load
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, 0, bnext);
+        if (t + 1 < ntiles) step(t + 1, 1, bnext);
     }
 
     // ---- normalise and store: lane holds column lc, dims dt*16 + 4*lg .. +3
@@ -278,10 +334,12 @@ template <int D, int GP>
 static hipError_t launch_prefill_g(const PrefillArgs& a, int total_rows, hipStream_t stream) {
     constexpr int kNW = 4, kCT = 2;
     constexpr int kRT = kNW * 16 * kCT / GP;
-    const long long tiles = (long long)total_rows / kRT + a.num_seqs;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<D, GP, kNW, kCT>), dim3((unsigned)tiles, a.num_kv_heads),
-                       dim3(kNW * kWave), 0, stream, a);
+    // an upper bound of the work items (sequence, kv head, row tile), rounded
+    // up to whole XCD shares
+    const long long items = ((long long)total_rows / kRT + a.num_seqs) * a.num_kv_heads;
+    const long long grid = (items + 7) / 8 * 8;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_kernel<D, GP, kNW, kCT>), dim3((unsigned)grid), dim3(kNW * kWave), 0, stream, a);
     return hipGetLastError();
 }
 
