@@ -117,6 +117,20 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int m = 0; m < kMs; ++m) qb[ct][m] = *reinterpret_cast<const uint4*>(qrow + 32 * m);
     }
+    // Scores are scaled inside the exponent, exp2(s * scale - m), with the
+    // running max taken over raw scores; for a negative scale q is negated
+    // (exact in bf16) so that the scale used is positive.
+    const float qscale = fabsf(a.scale_log2);
+    if (a.scale_log2 < 0.f) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+            for (int m = 0; m < kMs; ++m) {
+                qb[ct][m].x ^= 0x80008000u; qb[ct][m].y ^= 0x80008000u;
+                qb[ct][m].z ^= 0x80008000u; qb[ct][m].w ^= 0x80008000u;
+            }
+        }
+    }
 
     f32x4_t o[CT][kDt];
     float mrun[CT], lrun[CT];
@@ -147,28 +161,37 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
         return b;
     };
     static_assert(kKT == 4 * kBlockTokens, "a key tile is four blocks");
+    // Per-thread element offsets inside a block, fixed for the whole kernel
+    // (tiles start on block boundaries); which of the tile's four blocks a
+    // load reads is the same across a wave for K, and for V when D = 128.
+    constexpr size_t kBlkElems = (size_t)kBlockTokens * D;  // per kv head, times hkv_heads below
+    const size_t blk_stride = kBlkElems * hkv_heads;
+    uint32_t koff[kKChunks];
+    int kbi[kKChunks];
+#pragma unroll
+    for (int j = 0; j < kKChunks; ++j) {
+        const int q = tid + j * kNT;
+        const int key = q / (D / 8);
+        koff[j] = (uint32_t)(((key % kBlockTokens) * hkv_heads + hk) * D + (q % (D / 8)) * 8);
+        kbi[j] = __builtin_amdgcn_readfirstlane(key / kBlockTokens);
+    }
+    const int vk = tid < kVBlocks ? 4 * v_kg : 0;
+    const int vbi = D == 128 ? __builtin_amdgcn_readfirstlane(vk / kBlockTokens) : vk / kBlockTokens;
+    uint32_t voff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) voff[e] = (uint32_t)((((vk + e) % kBlockTokens) * hkv_heads + hk) * D + v_dc * 8);
     auto load_tile = [&](int t, int buf, int4 bq) __attribute__((always_inline)) {
-        const int t0 = t * kKT;
-        const int b4[4] = {bq.x, bq.y, bq.z, bq.w};
-        auto blk = [&](int key) {  // block of tile key 0..63, without dynamic indexing
-            const int j = key / kBlockTokens;
-            return j == 0 ? b4[0] : j == 1 ? b4[1] : j == 2 ? b4[2] : b4[3];
+        auto blk = [&](int j) {  // block j of the tile, without dynamic indexing
+            return j == 0 ? bq.x : j == 1 ? bq.y : j == 2 ? bq.z : bq.w;
         };
 #pragma unroll
         for (int j = 0; j < kKChunks; ++j) {
-            const int q = tid + j * kNT;
-            const int key = q / (D / 8);
-            const int ch = q % (D / 8);
-            kreg[buf][j] = *reinterpret_cast<const u32x4*>(
-                kcache + (((size_t)blk(key) * kBlockTokens + (t0 + key) % kBlockTokens) * hkv_heads + hk) * D + ch * 8);
+            const uint16_t* base = kcache + (size_t)blk(kbi[j]) * blk_stride;
+            kreg[buf][j] = *reinterpret_cast<const u32x4*>(base + koff[j]);
         }
-        const int vk = tid < kVBlocks ? 4 * v_kg : 0;
+        const uint16_t* vbase = vcache + (size_t)blk(vbi) * blk_stride;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vreg[buf][e] = *reinterpret_cast<const u32x4*>(
-                vcache + (((size_t)blk(vk + e) * kBlockTokens + (t0 + vk + e) % kBlockTokens) * hkv_heads + hk) * D +
-                v_dc * 8);
-        }
+        for (int e = 0; e < 4; ++e) vreg[buf][e] = *reinterpret_cast<const u32x4*>(vbase + voff[e]);
     };
     auto store_tile = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -184,7 +207,9 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
         // V^T column of this thread's 4 keys: within each group of 32 keys the
         // 4-key chunks are stored in the order 0,4,1,5,2,6,3,7, so that the
         // keys lane group g needs for a 32-key MFMA step (chunks g and g+4)
-        // are 16 contiguous bytes
+        // are 16 contiguous bytes.  Row r's 16-byte chunks are then permuted by
+        // XOR with (r / 16) % 8, which spreads these stores over the LDS banks
+        // (the reads of one MFMA step all share r / 16).
         const int xk = v_kg % 8;
         const int vcol = (v_kg / 8) * 32 + 4 * (xk < 4 ? 2 * xk : 2 * (xk - 4) + 1);
         // transpose the 4 keys x 8 dims block: dim e gets (k0, k1, k2, k3)
@@ -199,8 +224,10 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
                                         __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u));
             const uint2 od = make_uint2(__builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u),
                                         __builtin_amdgcn_perm(w3[j], w2[j], 0x07060302u));
-            *reinterpret_cast<uint2*>(&vt_lds[(v_dc * 8 + 2 * j) * kVP + vcol]) = ev;
-            *reinterpret_cast<uint2*>(&vt_lds[(v_dc * 8 + 2 * j + 1) * kVP + vcol]) = od;
+            const int r0e = v_dc * 8 + 2 * j;  // even row; the odd row is in the same 16-row band
+            const int sc = vcol ^ (8 * ((r0e >> 4) & 7));
+            *reinterpret_cast<uint2*>(&vt_lds[r0e * kVP + sc]) = ev;
+            *reinterpret_cast<uint2*>(&vt_lds[(r0e + 1) * kVP + sc]) = od;
         }
     };
 
@@ -235,18 +262,18 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
         uint4 pb[CT][2];  // B operands of the two 32-key P*V steps
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            float sv[4][4];
+            float sv[4][4];  // raw scores, -inf where masked
             float tmax = -INFINITY;
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = t0 + sb * 16 + 4 * lg + r;
-                    const float x = sacc[sb][ct][r] * a.scale_log2;
-                    sv[sb][r] = !masked || key <= col_pos[ct] ? x : -INFINITY;
+                    sv[sb][r] = !masked || key <= col_pos[ct] ? sacc[sb][ct][r] : -INFINITY;
                     tmax = fmaxf(tmax, sv[sb][r]);
                 }
             }
+            tmax *= qscale;
             // Lazy running max: raised only when a score exceeds it by more than
             // kSlack (log2 units), so exp2 stays <= 2^kSlack and the rescale of
             // the accumulators is rare.  Tile 0 holds key 0, visible to every
@@ -265,32 +292,35 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int dt = 0; dt < kDt; ++dt) o[ct][dt] *= alpha;
             }
-            const float mc = mrun[ct];
-            float psum = 0.f;
+            const float nm = -mrun[ct];
             float pv[4][4];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pv[sb][r] = fast_exp2(sv[sb][r] - mc);
-                    psum += pv[sb][r];
-                }
+                for (int r = 0; r < 4; ++r) pv[sb][r] = fast_exp2(fmaf(sv[sb][r], qscale, nm));
             }
-            lrun[ct] += psum;
+            float psum = lrun[ct];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 pb[ct][kk] = make_uint4(pack_bf16x2(pv[2 * kk][0], pv[2 * kk][1]),
                                         pack_bf16x2(pv[2 * kk][2], pv[2 * kk][3]),
                                         pack_bf16x2(pv[2 * kk + 1][0], pv[2 * kk + 1][1]),
                                         pack_bf16x2(pv[2 * kk + 1][2], pv[2 * kk + 1][3]));
+                // the normaliser sums the probabilities as rounded for P*V
+                psum = dot2_bf16(pb[ct][kk].x, 0x3F803F80u, psum);
+                psum = dot2_bf16(pb[ct][kk].y, 0x3F803F80u, psum);
+                psum = dot2_bf16(pb[ct][kk].z, 0x3F803F80u, psum);
+                psum = dot2_bf16(pb[ct][kk].w, 0x3F803F80u, psum);
             }
+            lrun[ct] = psum;
         }
         // ---- O^T += V^T P^T (32 keys per step)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int dt = 0; dt < kDt; ++dt) {
-                const uint4 va = *reinterpret_cast<const uint4*>(&vt_lds[(dt * 16 + lc) * kVP + 32 * kk + 8 * lg]);
+                const uint4 va = *reinterpret_cast<const uint4*>(
+                    &vt_lds[(dt * 16 + lc) * kVP + ((32 * kk + 8 * lg) ^ (8 * (dt & 7)))]);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) o[ct][dt] = mfma16x16x32_bf16(va, pb[ct][kk], o[ct][dt]);
             }
