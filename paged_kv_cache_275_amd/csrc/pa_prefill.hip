@@ -42,7 +42,7 @@ namespace pa {
 constexpr float kSlack = 8.0f;  // log2 units: lazy running max, exp2 <= 256
 
 template <int D, int GP, int NW, int CT>
-__global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NW * kWave, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int kCols = NW * 16 * CT;  // (row, head) columns per workgroup
     constexpr int kRT = kCols / GP;      // query rows per workgroup
     constexpr int kKT = 64;              // keys per tile
