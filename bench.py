@@ -1,8 +1,10 @@
 """Benchmark: one paged-attention step (KV append + decode) on one MI355X.
 
-A step is one pass of the hot path over one batch: pa_reshape_and_cache of
-the new tokens, then pa_decode over every sequence (and, for the mixed
-workload, pa_prefill_chunk over the prefill chunks first).  Inputs are the
+A step is one pass of the hot path over one batch: the KV append of the new
+tokens and decode attention over every sequence -- by default in one launch,
+pa_decode_append (append fused into the decode kernel); with --unfused as
+pa_reshape_and_cache then pa_decode.  For the mixed workload the prefill
+chunks' tokens go through pa_reshape_and_cache and pa_prefill_chunk first.  Inputs are the
 seeded synthetic workloads of paged_kv_cache_275_amd.workloads, resident in
 HBM before timing starts.  To time HBM rather than the 256 MB Infinity Cache,
 the step rotates over R independent copies of the KV pool, so each step's K/V
@@ -208,6 +210,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="independent KV pool copies")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append decode tokens with pa_reshape_and_cache, then pa_decode (default: pa_decode_append)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", action="store_true")
     ap.add_argument("--pmc-fetch")
@@ -262,14 +266,23 @@ def main():
         pre["out"] = torch.empty_like(pre["q"])
     stream = torch.cuda.current_stream(dev)
 
-    # arguments are checked once per pool copy; the loop only crosses the C ABI
+    # arguments are checked once per pool copy; the loop only crosses the C ABI.
+    # Default step: prefill tokens (if any) through pa_reshape_and_cache, then
+    # pa_decode_append, which appends each sequence's new token and attends in
+    # one kernel.  --unfused: every token through pa_reshape_and_cache, then
+    # pa_decode.
+    t_new, s_dec = k_new.shape[0], wl.num_seqs
+    n_sep = t_new if args.unfused else t_new - s_dec   # tokens appended by pa_reshape_and_cache
     calls = []
     for kc, vc in pools:
         calls.append({
-            "append": ops.bind_reshape_and_cache(k_new, v_new, kc, vc, slots),
+            "append": None if n_sep == 0 else ops.bind_reshape_and_cache(
+                k_new[:n_sep], v_new[:n_sep], kc, vc, slots[:n_sep]),
             "prefill": None if pre is None else ops.bind_prefill_chunk(
                 pre["out"], pre["q"], kc, vc, pre["bt"], pre["qsl"], pre["cl"], wl.scale),
-            "decode": ops.bind_decode(out, q, kc, vc, bt, cl, wl.scale, workspace=ws),
+            "decode": ops.bind_decode(out, q, kc, vc, bt, cl, wl.scale, workspace=ws) if args.unfused else
+            ops.bind_decode_append(out, q, k_new[t_new - s_dec:], v_new[t_new - s_dec:], kc, vc, bt, cl,
+                                   wl.scale, workspace=ws),
         })
 
     def new_events(n):
@@ -284,7 +297,8 @@ def main():
         c = calls[i % len(calls)]
         if ev is not None and ev[0] is not None:
             ev[0].record(stream)
-        c["append"]()
+        if c["append"] is not None:
+            c["append"]()
         if ev is not None and ev[1] is not None:
             ev[1].record(stream)
         if c["prefill"] is not None:
@@ -313,8 +327,9 @@ def main():
     pev, pkev = [p[0] for p in prof], [p[1] for p in prof]
     append_us, prefill_us, decode_us = span(pev, 0, 1), span(pev, 1, 2), span(pev, 2, 3)
     stream_us = span(pkev, 0, 1)
-    kernels = {"decode_stream_kernel": float(stream_us.mean()),
-               "reshape_and_cache_kernel": float(append_us.mean())}
+    kernels = {"decode_stream_kernel": float(stream_us.mean())}
+    if n_sep > 0:
+        kernels["reshape_and_cache_kernel"] = float(append_us.mean())
     if pre is not None:
         kernels["prefill_kernel"] = float(prefill_us.mean())
     dom = max(kernels, key=kernels.get)
@@ -377,11 +392,13 @@ def main():
             "context_tokens": int(wl.context_lens.sum()), "pool_blocks": wl.num_blocks,
             "seed": seed, "kv_bytes_per_step": kv_bytes, "pool_copies": len(pools),
             "prefill_rows": None if pre is None else int(wl.prefill.query_start_loc[-1]),
+            "decode_append": "separate pa_reshape_and_cache + pa_decode" if args.unfused else
+                             "fused (pa_decode_append)",
         },
         "timing_us": {
             "dominant_kernel_timed": pct(dom_us),
             "breakdown_steps": n_prof,
-            "append_call": pct(append_us),
+            "append_call": pct(append_us) if n_sep > 0 else None,
             "prefill_call": pct(prefill_us) if pre is not None else None,
             "decode_call": pct(decode_us),
             "decode_stream_kernel": pct(stream_us),

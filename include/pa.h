@@ -137,6 +137,37 @@ int pa_decode_timed(void *out, const void *q,
                     void *workspace, size_t workspace_bytes, void *stream,
                     void *kernel_start, void *kernel_stop);
 
+/*
+ * Decode step with the KV append fused in: for every sequence s with
+ * n = context_lens[s] >= 1, key[s] and value[s] ([num_seqs, num_kv_heads,
+ * head_dim]) are the new token's K and V at position n - 1.  They are written
+ * to k_cache/v_cache at that position's slot (block_tables[s, (n-1)/16],
+ * offset (n-1) % 16), and out is what pa_decode computes over positions
+ * 0..n-1, position n-1 included.  The result is that of pa_reshape_and_cache
+ * with slot_mapping[s] = that slot, followed by pa_decode, in one kernel
+ * launch (plus the split-context merge).  Sequences with n = 0 append nothing
+ * and get zero rows.  Same arguments, errors and workspace as pa_decode;
+ * key/value must be non-NULL (PA_EINVAL otherwise) and must not overlap the
+ * caches.  Position n-1's slot is overwritten whatever it held.
+ */
+int pa_decode_append(void *out, const void *q, const void *key, const void *value,
+                     void *k_cache, void *v_cache,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* pa_decode_append with the streaming kernel timed, as pa_decode_timed. */
+int pa_decode_append_timed(void *out, const void *q, const void *key, const void *value,
+                           void *k_cache, void *v_cache,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                           void *workspace, size_t workspace_bytes, void *stream,
+                           void *kernel_start, void *kernel_stop);
+
 /* Bytes of workspace pa_prefill_chunk needs (currently always 0). */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows,
                                  int32_t num_q_heads, int32_t head_dim,

@@ -139,21 +139,16 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
     return decode_ws_layout(gp, head_dim).total;
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-              int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, void* workspace,
-              size_t workspace_bytes, void* stream) {
-    return pa_decode_timed(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, workspace,
-                           workspace_bytes, stream, nullptr, nullptr);
-}
+namespace {
 
-int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, void* workspace,
-                    size_t workspace_bytes, void* stream, void* kernel_start, void* kernel_stop) {
+// pa_decode and its fused-append and timed variants: key/value non-null means
+// fused append (the caches are then written).
+int decode_impl(void* out, const void* q, const void* key, const void* value, const void* k_cache,
+                const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                void* workspace, size_t workspace_bytes, void* stream, void* kernel_start, void* kernel_stop,
+                bool fused) {
     int rc = check_dtype(dtype);
     if (rc) return rc;
     if (num_seqs < 0) return PA_EINVAL;
@@ -165,6 +160,7 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
     if (!isfinite(scale)) return PA_EINVAL;
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+    if (fused && (!key || !value)) return PA_EINVAL;
     if (num_seqs > pa::kDecodeMaxSeqs) return PA_EUNSUPPORTED;
     const int group = num_q_heads / num_kv_heads;
     const int gp = heads_per_wave(group);
@@ -178,6 +174,10 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
+    a.new_k = fused ? key : nullptr;
+    a.new_v = fused ? value : nullptr;
+    a.k_cache_w = fused ? const_cast<void*>(k_cache) : nullptr;
+    a.v_cache_w = fused ? const_cast<void*>(v_cache) : nullptr;
     a.ws_split = reinterpret_cast<pa::SplitNote*>(static_cast<char*>(workspace) + ws.split);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml);
     a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc);
@@ -202,6 +202,49 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
     hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(kernel_start), static_cast<hipEvent_t>(kernel_stop));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+}  // namespace
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                       workspace, workspace_bytes, stream, nullptr, nullptr, false);
+}
+
+int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream, void* kernel_start, void* kernel_stop) {
+    return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                       workspace, workspace_bytes, stream, kernel_start, kernel_stop, false);
+}
+
+int pa_decode_append(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                     void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                       workspace, workspace_bytes, stream, nullptr, nullptr, true);
+}
+
+int pa_decode_append_timed(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                           void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                           void* kernel_start, void* kernel_stop) {
+    return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                       workspace, workspace_bytes, stream, kernel_start, kernel_stop, true);
 }
 
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows, int32_t num_q_heads,

@@ -400,6 +400,29 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             }
         }
     }
+    if (a.new_k != nullptr && threadIdx.x < kWave) {
+        // Fused KV append: wave 0 of each workgroup copies the new token's K/V
+        // rows of some sequences into their cache slots (position N-1).  No
+        // wave of this kernel reads those slots: the units holding a new token
+        // take its rows from the inputs instead (see issue below), so the
+        // copies need no ordering against the attention.
+        constexpr int kRowVecsPerHead = D * (int)sizeof(T) / 16;
+        const int row_vecs = a.num_kv_heads * kRowVecsPerHead;
+        for (int sq = blockIdx.x; sq < S; sq += gridDim.x) {
+            const int nq = a.context_lens[sq];
+            if (nq <= 0) continue;
+            const int bq = a.block_tables[(size_t)sq * a.max_blocks_per_seq + (nq - 1) / kBlockTokens];
+            const size_t slot = (size_t)bq * kBlockTokens + (nq - 1) % kBlockTokens;
+            const uint4* ksrc = reinterpret_cast<const uint4*>(a.new_k) + (size_t)sq * row_vecs;
+            const uint4* vsrc = reinterpret_cast<const uint4*>(a.new_v) + (size_t)sq * row_vecs;
+            uint4* kdst = reinterpret_cast<uint4*>(a.k_cache_w) + slot * row_vecs;
+            uint4* vdst = reinterpret_cast<uint4*>(a.v_cache_w) + slot * row_vecs;
+            for (int i = threadIdx.x; i < row_vecs; i += kWave) {
+                kdst[i] = ksrc[i];
+                vdst[i] = vsrc[i];
+            }
+        }
+    }
     const long long NG = a.wave_groups;
     // wave index, made wave-uniform explicitly: everything the wave decides
     // (ranges, segment walk, branches) derives from it, and the compiler would
@@ -520,33 +543,53 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         const uint32_t hv = __builtin_amdgcn_readfirstlane(e.y);
         vld[st] = (int)(hv >> 16);
         const size_t base = ((size_t)b * kBlockTokens * hkv_heads + (hv & 0xFFFFu)) * D;
-        const T* vb = vbase + base + lane_off;
+        // rows of the block's two token halves (V, and K on the fp32 path); with
+        // a fused append, the block holding a sequence's new token (e.w = its
+        // input row) reads that token's rows from the inputs: the lane choice
+        // changes addresses only, never the number of loads
+        const uint32_t nrow = __builtin_amdgcn_readfirstlane(e.w);
+        const int noff = vld[st] - 1;  // the new token is the block's last valid one
+        const T* vb0 = vbase + base + lane_off;
+        const T* vb1 = vb0 + tok8_off;
+        const T* kt0 = kbase + base + lane_off;
+        const T* kt1 = kt0 + tok8_off;
+        if (nrow != 0xFFFFFFFFu) {
+            const size_t in_off = (size_t)nrow * D + dl * kE;
+            if (tg == noff) {
+                vb0 = reinterpret_cast<const T*>(a.new_v) + in_off;
+                kt0 = reinterpret_cast<const T*>(a.new_k) + in_off;
+            }
+            if (tg + 8 == noff) {
+                vb1 = reinterpret_cast<const T*>(a.new_v) + in_off;
+                kt1 = reinterpret_cast<const T*>(a.new_k) + in_off;
+            }
+        }
         if constexpr (kMfma) {
             const T* kb = kbase + base + kmf_off;
+            if (nrow != 0xFFFFFFFFu && mtok == noff)
+                kb = reinterpret_cast<const T*>(a.new_k) + (size_t)nrow * D + 8 * mrow;
 #pragma unroll
             for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = *reinterpret_cast<const uint4*>(kb + 32 * mm);
             // the unit's query rows travel with its K/V: no load outside the ring
             // ever has to be waited for (loads complete in issue order)
             const uint32_t qrow0 = __builtin_amdgcn_readfirstlane(e.z);
-            const uint32_t nvh = __builtin_amdgcn_readfirstlane(e.w);
-            const uint32_t hi = (uint32_t)mtok < nvh ? (uint32_t)mtok : 0u;
+            const uint32_t hi = mtok < nvh ? (uint32_t)mtok : 0u;
             const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)(qrow0 + hi) * D + 8 * mrow;
 #pragma unroll
             for (int mm = 0; mm < kMf; ++mm) qs[st][mm] = *reinterpret_cast<const uint4*>(qp + 32 * mm);
         } else {
-            const T* kb = kbase + base + lane_off;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
                 for (int c = 0; c < kVecs; ++c)
-                    kr[st][t][c] = *reinterpret_cast<const uint4*>(kb + t * tok8_off + c * 8 * kE);
+                    kr[st][t][c] = *reinterpret_cast<const uint4*>((t == 0 ? kt0 : kt1) + c * 8 * kE);
             }
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int c = 0; c < kVecs; ++c)
-                vr[st][t][c] = *reinterpret_cast<const uint4*>(vb + t * tok8_off + c * 8 * kE);
+                vr[st][t][c] = *reinterpret_cast<const uint4*>((t == 0 ? vb0 : vb1) + c * 8 * kE);
         }
     };
 
@@ -606,9 +649,12 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             const int b = a.block_tables[(size_t)s * a.max_blocks_per_seq + blk];
             const int valid = min(kBlockTokens, a.context_lens[s] - blk * kBlockTokens);
             // block id; kv head | valid tokens << 16; first query row of the
-            // head group; query heads present
+            // head group; input row of the new token if this block holds it
+            // (fused append), else ~0
+            const bool holds_new = a.new_k != nullptr && blk == pref[s + 1] - pref[s] - 1;
             tab[i] = make_uint4((uint32_t)b, (uint32_t)hk | ((uint32_t)valid << 16),
-                                (uint32_t)(s * a.num_q_heads + h0), (uint32_t)nvh);
+                                (uint32_t)(s * a.num_q_heads + h0),
+                                holds_new ? (uint32_t)(s * a.num_kv_heads + hk) : 0xFFFFFFFFu);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();

@@ -42,6 +42,12 @@ struct DecodeArgs {
     const void* v_cache;
     const int32_t* block_tables;
     const int32_t* context_lens;
+    // fused append (all null otherwise): each sequence's new token, [S, Hkv, D],
+    // written to the cache at position N-1 and read from here by the attention
+    const void* new_k;
+    const void* new_v;
+    void* k_cache_w;
+    void* v_cache_w;
     SplitNote* ws_split;   // [waves] split segment starting in each wave
     float* ws_ml;   // [waves, 2, GP, 2]  (running max in log2 units, sum)
     float* ws_acc;  // [waves, 2, GP, D]  unnormalised partial outputs

@@ -51,6 +51,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_timed.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
                                     ctypes.c_int, p, sz, p, p, p]
     lib.pa_decode_timed.restype = ctypes.c_int
+    lib.pa_decode_append.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
+                                     ctypes.c_int, p, sz, p]
+    lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_decode_append_timed.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
+                                           ctypes.c_int, p, sz, p, p, p]
+    lib.pa_decode_append_timed.restype = ctypes.c_int
     lib.pa_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_prefill_workspace_size.restype = sz
     lib.pa_prefill_chunk.argtypes = [p, p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32, i64,
@@ -214,6 +220,47 @@ def bind_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: flo
             _check(lib, "pa_decode", plain(*args))
         else:
             _check(lib, "pa_decode_timed", timed(*args, *kernel_events))
+    return call
+
+
+def _decode_append_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale, workspace,
+                        stream) -> tuple:
+    args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace, stream)
+    _need(key, "key", q.dtype, 3)
+    _need(value, "value", q.dtype, 3)
+    if tuple(key.shape) != (q.shape[0], k_cache.shape[2], q.shape[2]) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    return args[:2] + (key.data_ptr(), value.data_ptr()) + args[2:], ws
+
+
+def decode_append(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                  workspace=None, stream=None, kernel_events=None) -> None:
+    """Decode step with the KV append fused in (pa_decode_append): key/value
+    [S, Hkv, D] are each sequence's new token at position context_lens[s] - 1."""
+    lib = load_library()
+    args, _ = _decode_append_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale,
+                                  workspace, stream)
+    if kernel_events is None:
+        _check(lib, "pa_decode_append", lib.pa_decode_append(*args))
+    else:
+        _check(lib, "pa_decode_append_timed",
+               lib.pa_decode_append_timed(*args, *_event_handles(kernel_events)))
+
+
+def bind_decode_append(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                       workspace=None, stream=None):
+    """Check the arguments once; return f(kernel_events=None) that enqueues the
+    same fused decode step again (see bind_reshape_and_cache)."""
+    lib = load_library()
+    args, ws = _decode_append_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale,
+                                   workspace, stream)
+    plain, timed = lib.pa_decode_append, lib.pa_decode_append_timed
+
+    def call(kernel_events=None, _keep=ws):
+        if kernel_events is None:
+            _check(lib, "pa_decode_append", plain(*args))
+        else:
+            _check(lib, "pa_decode_append_timed", timed(*args, *kernel_events))
     return call
 
 

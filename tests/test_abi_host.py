@@ -25,7 +25,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = ops.header_functions()
     assert {"pa_reshape_and_cache", "pa_decode", "pa_prefill_chunk", "pa_decode_workspace_size",
-            "pa_prefill_workspace_size", "pa_status_string", "pa_decode_timed"} <= set(names)
+            "pa_prefill_workspace_size", "pa_status_string", "pa_decode_timed",
+            "pa_decode_append", "pa_decode_append_timed"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libpa.so does not export {n}"
     out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
@@ -38,6 +39,18 @@ def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4):
         assert lib.pa_status_string(code).startswith(b"PA_")
     assert lib.pa_status_string(123) == b"unknown pa_status"
+
+
+def _decode_append(lib, timed=False, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=4, cl=FAKE, s=2, hq=8,
+             hkv=2, d=128, bs=16, nb=64, scale=0.1, dtype=ops.PA_BF16, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    args = (a["out"], a["q"], a["key"], a["value"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["s"],
+            a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+            a["stream"])
+    if timed:
+        return lib.pa_decode_append_timed(*args, FAKE, FAKE)
+    return lib.pa_decode_append(*args)
 
 
 def _decode(lib, timed=False, **kw):
@@ -74,6 +87,14 @@ def _decode(lib, timed=False, **kw):
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
     assert _decode(lib, timed=True, **kw) == code
+    assert _decode_append(lib, **kw) == code
+    assert _decode_append(lib, timed=True, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(key=None), dict(value=None)])
+def test_decode_append_needs_new_tokens(lib, kw):
+    assert _decode_append(lib, **kw) == ops.PA_EINVAL
+    assert _decode_append(lib, timed=True, **kw) == ops.PA_EINVAL
 
 
 def test_decode_empty_batch_is_noop(lib):

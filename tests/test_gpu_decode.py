@@ -204,3 +204,88 @@ def test_decode_launch_shapes(waves, monkeypatch):
     _check_workload(wl, f"waves={waves}")
     wl = W.make_workload("long_skewed", seed=22, num_seqs=2)
     _check_workload(wl, f"waves={waves}/long")
+
+
+# ---------------------------------------------------------------- fused append
+def _run_fused(wl):
+    """pa_decode_append with the decode tokens (the last num_seqs new tokens);
+    prefill tokens, if any, are appended first with pa_reshape_and_cache."""
+    dw = DevWorkload(wl)
+    s = wl.num_seqs
+    t = wl.k_new.shape[0]
+    if t > s:
+        ops.reshape_and_cache(dw.k_new[:t - s], dw.v_new[:t - s], dw.k_cache, dw.v_cache,
+                              dw.slot_mapping[:t - s])
+    ops.decode_append(dw.out, dw.q, dw.k_new[t - s:], dw.v_new[t - s:], dw.k_cache, dw.v_cache,
+                      dw.block_tables, dw.context_lens, wl.scale)
+    torch.cuda.synchronize()
+    return dw
+
+
+def _check_fused(wl, label):
+    print(f"[gpu] fused {label}: S={wl.num_seqs} sumN={int(wl.context_lens.sum())}", flush=True)
+    dw = _run_fused(wl)
+    kc, vc = _oracle_pool_after_append(wl)
+    assert to_host(dw.k_cache).tobytes() == kc.tobytes(), f"{label}: K cache differs"
+    assert to_host(dw.v_cache).tobytes() == vc.tobytes(), f"{label}: V cache differs"
+    ref = oracle.decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale)
+    mx, rel = assert_attention_close(widen_dev(dw.out), ref, wl.dtype, f"fused {label}")
+    print(f"[gpu] fused {label}: max-abs {mx:.3e} row-rel {rel:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name,num_seqs", [("tiny_fp32", None), ("qwen3_0p6b", 6), ("llama3_8b", 8),
+                                           ("long_skewed", 2), ("mixed_prefill", 6), ("llama3_8b", None)])
+def test_decode_append_equals_append_then_decode(name, num_seqs):
+    """Fused KV append + decode: the whole pool bit for bit as pa_reshape_and_cache
+    leaves it, and attention within tolerance of the oracle."""
+    seed = W.CONFIG_NAMES.index(name) + 300
+    _check_fused(W.make_workload(name, seed=seed, num_seqs=num_seqs), f"{name}/{num_seqs}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_append_single_token_returns_new_v(dtype):
+    """A context of one token is the new token alone: out equals its value row
+    exactly, read from the input (its cache slot held NaN before the call)."""
+    name = "tiny_fp32" if dtype == "f32" else "llama3_8b"
+    wl = W.make_workload(name, seed=41, num_seqs=4)
+    wl.context_lens[:] = 1
+    t = wl.k_new.shape[0]
+    for s in range(wl.num_seqs):
+        wl.slot_mapping[t - wl.num_seqs + s] = int(wl.block_tables[s, 0]) * 16
+    dw = _run_fused(wl)
+    got = to_host(dw.out)
+    hq, hkv = wl.num_q_heads, wl.num_kv_heads
+    for h in range(hq):
+        np.testing.assert_array_equal(got[:, h], wl.v_new[t - wl.num_seqs:, h // (hq // hkv)])
+
+
+def test_decode_append_block_boundaries_and_empty():
+    """New tokens at the first and last slot of a block, and a sequence with no
+    tokens (nothing appended, zero row)."""
+    rng = np.random.default_rng(77)
+    hq, hkv, d = 32, 8, 128
+    lens = [1, 15, 16, 17, 32, 33, 48, 0, 5]
+    q, kc, vc, bt, lens = _random_bf16_case(rng, hq, hkv, d, lens, spare_blocks=8)
+    s = len(lens)
+    # the new tokens' slots must not hold history: poison them, keep the rows aside
+    key = _bf16_bits(rng, (s, hkv, d))
+    value = _bf16_bits(rng, (s, hkv, d))
+    slots = np.array([int(bt[i, (n - 1) // 16]) * 16 + (n - 1) % 16 if n > 0 else -1
+                      for i, n in enumerate(lens)], np.int32)
+    for i, sl in enumerate(slots):
+        if sl >= 0:
+            kc.reshape(-1, hkv, d)[sl] = 0x7FC0
+            vc.reshape(-1, hkv, d)[sl] = 0x7FC0
+    from tests._gpu import to_dev
+    dkc, dvc = to_dev(kc), to_dev(vc)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.decode_append(out, to_dev(q), to_dev(key), to_dev(value), dkc, dvc, to_dev(bt), to_dev(lens), 0.088)
+    torch.cuda.synchronize()
+    okc, ovc = kc.copy(), vc.copy()
+    oracle.reshape_and_cache(key, value, okc, ovc, slots)
+    assert to_host(dkc).tobytes() == okc.tobytes()
+    assert to_host(dvc).tobytes() == ovc.tobytes()
+    got = widen_dev(out)
+    assert np.all(got[7] == 0.0)
+    ref = oracle.decode(q, okc, ovc, bt, lens, 0.088)
+    assert_attention_close(got, ref, "bf16", "fused boundaries")
