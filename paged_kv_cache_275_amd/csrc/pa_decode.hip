@@ -267,46 +267,69 @@ __device__ __forceinline__ void store_run(OutT* dst, const float (&v)[CH], float
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: row_shr 1, 2, 4, 8 within
+// each 16-lane row, then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then the first two rows' total into rows 2 and 3
+// (row_bcast:31).  Lanes without a source read 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_src_i32(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWMASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_scan_incl(int x) {
+    x += dpp_src_i32<0x111, 0xF>(x);
+    x += dpp_src_i32<0x112, 0xF>(x);
+    x += dpp_src_i32<0x114, 0xF>(x);
+    x += dpp_src_i32<0x118, 0xF>(x);
+    x += dpp_src_i32<0x142, 0xA>(x);
+    x += dpp_src_i32<0x143, 0xC>(x);
+    return x;
+}
+
 // Work is measured in TICKS: every unit costs unit_ticks, and every segment
 // adds switch_ticks for the work of closing it (reduction, stores, a fresh
 // running max).  pref[s] = blocks of sequences before s and tpref[s] = ticks of
 // one head group of every sequence before s, computed by all NT threads of the
-// workgroup (Hillis-Steele scan of per-thread chunk sums).
+// workgroup: per-thread sums over a chunk of sequences, a scan within each
+// wave, and one barrier to add the totals of the waves before.
 template <int NT>
-__device__ void prefix_blocks(int* pref, int* tpref, int2* scratch, const int32_t* __restrict__ ctx, int S,
+__device__ void prefix_blocks(int* pref, int* tpref, int2* wave_tot, const int32_t* __restrict__ ctx, int S,
                               int unit_ticks, int switch_ticks) {
+    constexpr int NW = NT / kWave;
     const int t = threadIdx.x;
+    const int w = t / kWave;
     const int chunk = (S + NT - 1) / NT;
     const int lo = min(S, t * chunk);
     const int hi = min(S, lo + chunk);
     auto nblk = [&](int s) { return (ctx[s] + kBlockTokens - 1) / kBlockTokens; };
     auto ticks = [&](int nb) { return nb * unit_ticks + (nb > 0 ? switch_ticks : 0); };
-    int2 sum = make_int2(0, 0);
+    int sx = 0, sy = 0;
     for (int s = lo; s < hi; ++s) {
         const int nb = nblk(s);
-        sum.x += nb;
-        sum.y += ticks(nb);
+        sx += nb;
+        sy += ticks(nb);
     }
-    scratch[t] = sum;
+    const int ix = wave_scan_incl(sx), iy = wave_scan_incl(sy);
+    if ((t & (kWave - 1)) == kWave - 1) wave_tot[w] = make_int2(ix, iy);
     __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-        const int2 v = t >= off ? scratch[t - off] : make_int2(0, 0);
-        __syncthreads();
-        scratch[t].x += v.x;
-        scratch[t].y += v.y;
-        __syncthreads();
+    int ox = 0, oy = 0;
+#pragma unroll
+    for (int k = 0; k < NW - 1; ++k) {
+        if (k < w) {
+            ox += wave_tot[k].x;
+            oy += wave_tot[k].y;
+        }
     }
-    int2 run = make_int2(scratch[t].x - sum.x, scratch[t].y - sum.y);  // exclusive prefix of the chunk
+    int rx = ox + ix - sx, ry = oy + iy - sy;  // exclusive prefix of this thread's chunk
     for (int s = lo; s < hi; ++s) {
-        pref[s] = run.x;
-        tpref[s] = run.y;
+        pref[s] = rx;
+        tpref[s] = ry;
         const int nb = nblk(s);
-        run.x += nb;
-        run.y += ticks(nb);
+        rx += nb;
+        ry += ticks(nb);
     }
     if (t == NT - 1) {
-        pref[S] = scratch[t].x;
-        tpref[S] = scratch[t].y;
+        pref[S] = rx;
+        tpref[S] = ry;
     }
 }
 
@@ -374,7 +397,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     constexpr int kE = G::kE;
 
     extern __shared__ int smem[];
-    __shared__ int2 scan_scratch[NW * kWave];
+    __shared__ int2 scan_scratch[NW];
     const int S = a.num_seqs;
     int* pref = smem;
     int* tpref = smem + ((S + 1 + 3) & ~3);
