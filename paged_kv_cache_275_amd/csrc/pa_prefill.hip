@@ -42,7 +42,7 @@ namespace pa {
 constexpr float kSlack = 8.0f;  // log2 units: lazy running max, exp2 <= 256
 
 template <int D, int GP, int NW, int CT>
-__global__ __launch_bounds__(NW * kWave, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs a) {
     constexpr int kCols = NW * 16 * CT;  // (row, head) columns per workgroup
     constexpr int kRT = kCols / GP;      // query rows per workgroup
     constexpr int kKT = 64;              // keys per tile
@@ -191,7 +191,11 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_kernel(PrefillArgs a) {
         }
         const uint16_t* vbase = vcache + (size_t)blk(vbi) * blk_stride;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[buf][e] = *reinterpret_cast<const u32x4*>(vbase + voff[e]);
+        for (int e = 0; e < 4; ++e) {
+            // waves past the V blocks load nothing (uniform per wave: kVBlocks is
+            // a multiple of the wave size)
+            if (kVBlocks >= kNT || tid < kVBlocks) vreg[buf][e] = *reinterpret_cast<const u32x4*>(vbase + voff[e]);
+        }
     };
     auto store_tile = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------- launchers
 template <int D, int GP>
 static hipError_t launch_prefill_g(const PrefillArgs& a, int total_rows, hipStream_t stream) {
-    constexpr int kNW = 4, kCT = 2;
+    constexpr int kNW = 8, kCT = 2;
     constexpr int kRT = kNW * 16 * kCT / GP;
     // an upper bound of the work items (sequence, kv head, row tile), rounded
     // up to whole XCD shares
