@@ -207,7 +207,13 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
         // keys past the context: V is zero (the slots may hold anything)
         u32x4 vv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = t * kKT + 4 * v_kg + e < n ? vreg[buf][e] : u32x4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < 4; ++e) vv[e] = vreg[buf][e];
+        if (t * kKT + kKT > n) {  // uniform: only the tile that reaches past the context
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (t * kKT + 4 * v_kg + e >= n) vv[e] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
         // V^T column of this thread's 4 keys: within each group of 32 keys the
         // 4-key chunks are stored in the order 0,4,1,5,2,6,3,7, so that the
         // keys lane group g needs for a 32-key MFMA step (chunks g and g+4)
@@ -238,6 +244,8 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
     // Tile t uses register buffer t % 2.  The step is called with a literal
     // buffer index (the loop runs over pairs of tiles) so that the buffers stay
     // in registers.
+    // tiles [0, tmask) lie entirely at or before the first row's position
+    const int tmask = pos0 >= kKT - 1 ? (pos0 - (kKT - 1)) / kKT + 1 : 0;
     auto step = [&](const int t, const int buf, int4& bn) __attribute__((always_inline)) {
         __syncthreads();  // the previous tile is no longer being read
         store_tile(t, buf);
@@ -246,8 +254,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
         bn = tile_blocks(min(t + 3, ntiles - 1));     // requested a step before it is needed
         const int t0 = t * kKT;
         // every key of this tile is visible to every row of the workgroup
-        // unless the tile reaches past the first row's position
-        const bool masked = t0 + kKT - 1 > pos0;
+        // unless the tile reaches past the first row's position (the last
+        // tile or two of a row tile)
+        const bool masked = t >= tmask;
 
         // ---- S^T = K Q^T for the four 16-key subtiles
         f32x4_t sacc[4][CT];
@@ -262,6 +271,19 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
                 for (int ct = 0; ct < CT; ++ct) sacc[sb][ct] = mfma16x16x32_bf16(ka, qb[ct][m], sacc[sb][ct]);
             }
         }
+        // ---- causal mask, only on tiles that reach past the first row (uniform)
+        if (__builtin_expect(masked, 0)) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (t0 + sb * 16 + 4 * lg + r > col_pos[ct]) sacc[sb][ct][r] = -INFINITY;
+                    }
+                }
+            }
+        }
         // ---- online softmax per column
         uint4 pb[CT][2];  // B operands of the two 32-key P*V steps
 #pragma unroll
@@ -272,8 +294,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
             for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int key = t0 + sb * 16 + 4 * lg + r;
-                    sv[sb][r] = !masked || key <= col_pos[ct] ? sacc[sb][ct][r] : -INFINITY;
+                    sv[sb][r] = sacc[sb][ct][r];
                     tmax = fmaxf(tmax, sv[sb][r]);
                 }
             }
