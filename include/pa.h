@@ -68,7 +68,8 @@ typedef enum {
     PA_EINVAL = -1,       /* an argument is out of its documented range */
     PA_EUNSUPPORTED = -2, /* valid, but a shape or dtype this build does not handle */
     PA_EWORKSPACE = -3,   /* workspace pointer NULL or smaller than required */
-    PA_ELAUNCH = -4       /* the HIP runtime refused a launch */
+    PA_ELAUNCH = -4,      /* the HIP runtime refused a launch */
+    PA_ENOMEM = -5        /* block manager: not enough free blocks (nothing changed) */
 } pa_status;
 
 /*
@@ -193,6 +194,69 @@ int pa_prefill_chunk(void *out, const void *q,
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Copy on write.  For every pair p < num_pairs, block pairs[2p+1] of k_cache
+ * and of v_cache becomes a bit copy of block pairs[2p] (all block_size slots,
+ * all heads).  pairs is a DEVICE array [num_pairs, 2] of int32 block ids below
+ * num_blocks; destinations must be distinct and must not be sources of the
+ * same call (the copies run concurrently).  Used when a block shared by
+ * several sequences (a common prompt prefix, page "vllm-v0 版本介绍", section
+ * 为什么需要推理框架？, PagedAttention item) is about to be written by one of
+ * them; pa_bm_append_batch reports such pairs.  num_pairs == 0 is a no-op.
+ */
+int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int64_t num_blocks, pa_dtype dtype, void *stream);
+
+/*
+ * Host block manager (CPU only, no device memory): hands out the pool's block
+ * ids to sequences and builds the block tables, context lengths and slot
+ * mappings the kernels above take.  A sequence gets a new block only when its
+ * last one is full and returns all of them when it ends (page "轻量级的vLLM",
+ * sections 核心机制一：分页 KV Cache and 核心机制二：连续批处理).  A forked
+ * sequence shares every block of its parent (reference counted); the first
+ * write into a shared, partly filled last block moves the writer to a fresh
+ * copy (reported as a (src, dst) pair for pa_copy_blocks).
+ * Policy: free blocks form a stack, block 0 on top at creation; allocation
+ * pops, release pushes; a sequence releases its blocks last to first.  A call
+ * that fails changes nothing.  Not thread safe: one manager per thread.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* NULL if num_blocks is not in [1, INT32_MAX / 16] or block_size != 16. */
+pa_block_manager *pa_bm_create(int64_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager *m);
+/* Free blocks (-1 for NULL). */
+int64_t pa_bm_num_free(const pa_block_manager *m);
+/* Reference count of a block (0 = free), -1 when out of range. */
+int32_t pa_bm_refcount(const pa_block_manager *m, int32_t block);
+/* A new sequence holding num_tokens >= 0 tokens (their K/V are written by the
+ * caller, e.g. pa_reshape_and_cache over the slots of pa_bm_batch_tables).
+ * PA_EINVAL if seq_id exists, PA_ENOMEM if ceil(num_tokens/16) blocks are not
+ * free. */
+int pa_bm_add_sequence(pa_block_manager *m, int64_t seq_id, int64_t num_tokens);
+/* child_id starts as a copy of parent_id sharing all its blocks. */
+int pa_bm_fork(pa_block_manager *m, int64_t parent_id, int64_t child_id);
+/* The sequence ends; blocks whose count drops to 0 are freed. */
+int pa_bm_free(pa_block_manager *m, int64_t seq_id);
+/* Tokens held by a sequence, -1 if unknown. */
+int64_t pa_bm_num_tokens(const pa_block_manager *m, int64_t seq_id);
+/*
+ * One new token for each of the n distinct sequences seq_ids[i]: slot_mapping[i]
+ * receives its slot (block * 16 + offset).  Copy-on-write pairs (src, dst) go
+ * to copies[2*k], copies[2*k+1], k < *num_copies <= max_copies; apply them
+ * (pa_copy_blocks) before writing the new tokens.  PA_EINVAL for unknown or
+ * repeated ids or too little copy room, PA_ENOMEM if the blocks needed are not
+ * free; in both cases nothing changes.
+ */
+int pa_bm_append_batch(pa_block_manager *m, const int64_t *seq_ids, int32_t n, int32_t *slot_mapping,
+                       int32_t *copies, int32_t max_copies, int32_t *num_copies);
+/* Rows of block_tables [n, max_blocks_per_seq] (padded with -1) and
+ * context_lens [n] for seq_ids, host arrays; PA_EINVAL if a sequence is unknown
+ * or holds more than max_blocks_per_seq blocks. */
+int pa_bm_batch_tables(const pa_block_manager *m, const int64_t *seq_ids, int32_t n, int32_t *block_tables,
+                       int32_t max_blocks_per_seq, int32_t *context_lens);
 
 /* Static, human-readable text for a pa_status value. */
 const char *pa_status_string(int status);

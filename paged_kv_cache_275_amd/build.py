@@ -39,9 +39,10 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link libpa.so; returns the library path."""
+    """Compile every csrc/*.hip (and the host-only csrc/*.cpp) and link libpa.so;
+    returns the library path."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"

@@ -107,6 +107,7 @@ const char* pa_status_string(int status) {
         case PA_EUNSUPPORTED: return "PA_EUNSUPPORTED: shape or dtype not supported by this build";
         case PA_EWORKSPACE: return "PA_EWORKSPACE: workspace missing or too small";
         case PA_ELAUNCH: return "PA_ELAUNCH: the HIP runtime refused a kernel launch";
+        case PA_ENOMEM: return "PA_ENOMEM: not enough free KV blocks";
         default: return "unknown pa_status";
     }
 }
@@ -126,6 +127,22 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
     if (row_bytes > INT32_MAX) return PA_EUNSUPPORTED;
     hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
                                                 (int)row_bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
+    int rc = check_dtype(dtype);
+    if (rc) return rc;
+    if (num_pairs < 0) return PA_EINVAL;
+    rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
+    if (rc) return rc;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !pairs) return PA_EINVAL;
+    const long long block_bytes = (long long)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+    if (block_bytes > INT32_MAX) return PA_EUNSUPPORTED;
+    hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, (int)block_bytes,
+                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 

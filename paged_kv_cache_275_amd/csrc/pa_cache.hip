@@ -45,4 +45,33 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
     return hipGetLastError();
 }
 
+// Copy-on-write support: for every pair (src, dst) in pairs[n][2], block dst
+// of both caches becomes a bit copy of block src.  Each thread moves one
+// 16-byte vector.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs, int num_pairs,
+                                                          int block_vecs) {
+    const long long per_tensor = (long long)num_pairs * block_vecs;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * per_tensor;
+         i += (long long)gridDim.x * blockDim.x) {
+        const bool is_v = i >= per_tensor;
+        const long long j = is_v ? i - per_tensor : i;
+        const int p = (int)(j / block_vecs);
+        const int vec = (int)(j % block_vecs);
+        uint4* cache = is_v ? v_cache : k_cache;
+        cache[(long long)pairs[2 * p + 1] * block_vecs + vec] = cache[(long long)pairs[2 * p] * block_vecs + vec];
+    }
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int block_bytes,
+                              hipStream_t stream) {
+    const int block_vecs = block_bytes / 16;
+    const long long total = 2LL * num_pairs * block_vecs;
+    long long blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint4*>(k_cache),
+                       static_cast<uint4*>(v_cache), pairs, num_pairs, block_vecs);
+    return hipGetLastError();
+}
+
 }  // namespace pa

@@ -93,5 +93,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int num_tokens, int row_bytes,
                                     hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int block_bytes,
+                              hipStream_t stream);
 
 }  // namespace pa

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "pa.h")
 
 PA_F32 = 0
 PA_BF16 = 1
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH = 0, -1, -2, -3, -4
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH, PA_ENOMEM = 0, -1, -2, -3, -4, -5
 BLOCK_SIZE = 16
 
 _lib: Optional[ctypes.CDLL] = None
