@@ -128,6 +128,52 @@ def cpu_baseline(wl, budget_s: float):
     }
 
 
+def extras(wl, kc, vc, stream):
+    """Measurements of the block-management row, after (outside) the timed region:
+    the host manager's per-step work for this batch (one append per sequence,
+    then the batch's tables), and pa_copy_blocks bandwidth on 1024 blocks."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_275_amd.blocks import BlockManager, copy_blocks
+    out = {}
+    nb, s = wl.num_blocks, wl.num_seqs
+    mb = wl.max_blocks_per_seq
+    m = BlockManager(nb)
+    ids = list(range(s))
+    for i, n in enumerate(wl.context_lens.tolist()):
+        m.add_sequence(i, max(0, n - 64))          # leave room to append 64 tokens each
+    steps = 64
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        m.append_batch(ids)
+        m.batch_tables(ids, mb)
+    host_us = (time.perf_counter() - t0) / steps * 1e6
+    m.close()
+    out["block_manager_step_us"] = round(host_us, 2)
+    out["block_manager_step_note"] = (f"pa_bm_append_batch + pa_bm_batch_tables for {s} sequences "
+                                      "(host C++, through ctypes), mean of 64 steps")
+    npairs = min(1024, nb // 2)
+    perm = np.random.default_rng(0).permutation(nb)
+    pairs = torch.from_numpy(np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).astype(np.int32)).to(kc.device)
+    for _ in range(3):
+        copy_blocks(kc, vc, pairs)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    reps = 20
+    for _ in range(reps):
+        copy_blocks(kc, vc, pairs)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    block_bytes = kc[0].numel() * kc.element_size()
+    moved = 2 * 2 * npairs * block_bytes                      # K and V, read + write
+    out["copy_blocks_us"] = round(us, 2)
+    out["copy_blocks_gbs"] = round(moved / (us * 1e-6) / 1e9, 1)
+    out["copy_blocks_note"] = f"{npairs} block pairs of K and V ({block_bytes} B each), read + write bytes"
+    return out
+
+
 def prefill_flops(wl) -> int:
     """Algorithmic flops of the prefill chunks: 4*D per (query head, causal pair)."""
     p = wl.prefill
@@ -409,6 +455,7 @@ def main():
     if pre is not None:
         pf = prefill_flops(wl)
         res["timing_us"]["prefill_tflops"] = round(pf / (float(prefill_us.mean()) * 1e-6) / 1e12, 2)
+    res["extras"] = extras(wl, pools[0][0], pools[0][1], stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(res), flush=True)
