@@ -169,6 +169,30 @@ int pa_decode_append_timed(void *out, const void *q, const void *key, const void
                            void *workspace, size_t workspace_bytes, void *stream,
                            void *kernel_start, void *kernel_stop);
 
+/*
+ * The decode step as a HIP graph, for callers that repeat it on fixed buffers
+ * (the CUDA-graph-style launch the pages list among an engine's speed-ups:
+ * page "vllm-v0 版本介绍", section 为什么需要推理框架？, item 3).
+ * Records what pa_decode_append(<same arguments>) enqueues into a graph and
+ * returns its executable instance in *graph_exec (caller owns it: release with
+ * pa_graph_destroy).  The pointers and sizes are baked in; what the buffers
+ * hold may change between launches (new q/key/value rows, tables, lengths, as
+ * long as the shapes and num_seqs stay the same).  Nothing is run by this
+ * call.  num_seqs must be > 0.  Errors as pa_decode_append; PA_ELAUNCH if the
+ * runtime refuses the capture or the instantiation.
+ */
+int pa_decode_append_graph(void **graph_exec, void *out, const void *q, const void *key,
+                           const void *value, void *k_cache, void *v_cache,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                           void *workspace, size_t workspace_bytes);
+/* Enqueue a graph from pa_decode_append_graph on stream (NULL = default). */
+int pa_graph_launch(void *graph_exec, void *stream);
+/* Release a graph instance (NULL is a no-op). */
+int pa_graph_destroy(void *graph_exec);
+
 /* Bytes of workspace pa_prefill_chunk needs (currently always 0). */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows,
                                  int32_t num_q_heads, int32_t head_dim,

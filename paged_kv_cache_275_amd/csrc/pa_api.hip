@@ -165,7 +165,7 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                 int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
                 void* workspace, size_t workspace_bytes, void* stream, void* kernel_start, void* kernel_stop,
-                bool fused) {
+                bool fused, bool launch = true) {
     int rc = check_dtype(dtype);
     if (rc) return rc;
     if (num_seqs < 0) return PA_EINVAL;
@@ -183,6 +183,7 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     const int gp = heads_per_wave(group);
     const DecodeWsLayout ws = decode_ws_layout(gp, head_dim);
     if (workspace == nullptr || workspace_bytes < ws.total) return PA_EWORKSPACE;
+    if (!launch) return PA_OK;  // arguments checked only
 
     pa::DecodeArgs a;
     a.out = out;
@@ -262,6 +263,56 @@ int pa_decode_append_timed(void* out, const void* q, const void* key, const void
     return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                        workspace, workspace_bytes, stream, kernel_start, kernel_stop, true);
+}
+
+int pa_decode_append_graph(void** graph_exec, void* out, const void* q, const void* key, const void* value,
+                           void* k_cache, void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes) {
+    if (!graph_exec) return PA_EINVAL;
+    *graph_exec = nullptr;
+    if (num_seqs <= 0) return PA_EINVAL;  // an empty graph is of no use
+    int rc = decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                         workspace, workspace_bytes, nullptr, nullptr, nullptr, true, false);
+    if (rc != PA_OK) return rc;
+    // Record the launches on a private stream (default priority) in capture
+    // mode, then instantiate.
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return PA_ELAUNCH;
+    rc = PA_ELAUNCH;
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+        rc = decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                         workspace, workspace_bytes, cs, nullptr, nullptr, true);
+        const hipError_t e = hipStreamEndCapture(cs, &graph);
+        if (rc == PA_OK && e != hipSuccess) rc = PA_ELAUNCH;
+    }
+    if (rc == PA_OK) {
+        hipGraphExec_t ge = nullptr;
+        if (hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0) == hipSuccess) {
+            *graph_exec = ge;
+        } else {
+            rc = PA_ELAUNCH;
+        }
+    }
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cs);
+    return rc;
+}
+
+int pa_graph_launch(void* graph_exec, void* stream) {
+    if (!graph_exec) return PA_EINVAL;
+    return hipGraphLaunch(static_cast<hipGraphExec_t>(graph_exec), static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PA_OK
+               : PA_ELAUNCH;
+}
+
+int pa_graph_destroy(void* graph_exec) {
+    if (!graph_exec) return PA_OK;
+    return hipGraphExecDestroy(static_cast<hipGraphExec_t>(graph_exec)) == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows, int32_t num_q_heads,

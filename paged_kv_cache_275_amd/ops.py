@@ -57,6 +57,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_append_timed.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
                                            ctypes.c_int, p, sz, p, p, p]
     lib.pa_decode_append_timed.restype = ctypes.c_int
+    lib.pa_decode_append_graph.argtypes = [ctypes.POINTER(p), p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32,
+                                           i32, i64, f32, ctypes.c_int, p, sz]
+    lib.pa_decode_append_graph.restype = ctypes.c_int
+    lib.pa_graph_launch.argtypes = [p, p]
+    lib.pa_graph_launch.restype = ctypes.c_int
+    lib.pa_graph_destroy.argtypes = [p]
+    lib.pa_graph_destroy.restype = ctypes.c_int
     lib.pa_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_prefill_workspace_size.restype = sz
     lib.pa_prefill_chunk.argtypes = [p, p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32, i64,
@@ -262,6 +269,36 @@ def bind_decode_append(out, q, key, value, k_cache, v_cache, block_tables, conte
         else:
             _check(lib, "pa_decode_append_timed", timed(*args, *kernel_events))
     return call
+
+
+class DecodeStepGraph:
+    """pa_decode_append recorded once as a HIP graph (pa_decode_append_graph);
+    launch() replays it on the current (or given) stream.  The tensors are
+    kept alive by this object; refill their contents between launches."""
+
+    def __init__(self, out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                 workspace=None):
+        lib = load_library()
+        args, ws = _decode_append_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale,
+                                       workspace, None)
+        self._keep = (out, q, key, value, k_cache, v_cache, block_tables, context_lens, ws)
+        self._lib = lib
+        self._h = ctypes.c_void_p()
+        _check(lib, "pa_decode_append_graph", lib.pa_decode_append_graph(ctypes.byref(self._h), *args[:-1]))
+        self._device = q.device
+
+    def launch(self, stream=None) -> None:
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self._device)
+        _check(self._lib, "pa_graph_launch", self._lib.pa_graph_launch(self._h, s.cuda_stream))
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_graph_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        self.close()
 
 
 def prefill_workspace_size(num_seqs, total_query_rows, num_q_heads, head_dim, max_blocks_per_seq,

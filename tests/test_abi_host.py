@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol(lib):
     names = ops.header_functions()
     assert {"pa_reshape_and_cache", "pa_decode", "pa_prefill_chunk", "pa_decode_workspace_size",
             "pa_prefill_workspace_size", "pa_status_string", "pa_decode_timed",
-            "pa_decode_append", "pa_decode_append_timed"} <= set(names)
+            "pa_decode_append", "pa_decode_append_timed", "pa_decode_append_graph", "pa_graph_launch",
+            "pa_graph_destroy", "pa_copy_blocks", "pa_bm_create", "pa_bm_append_batch"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libpa.so does not export {n}"
     out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
@@ -89,6 +90,22 @@ def test_decode_rejects(lib, kw, code):
     assert _decode(lib, timed=True, **kw) == code
     assert _decode_append(lib, **kw) == code
     assert _decode_append(lib, timed=True, **kw) == code
+
+
+def test_graph_entry_points_reject_without_launching(lib):
+    h = ctypes.c_void_p()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 8, 2, 128, 16, 64, 0.1, ops.PA_BF16, FAKE,
+            1 << 30]
+    assert lib.pa_decode_append_graph(None, *args) == ops.PA_EINVAL
+    bad = list(args); bad[9] = 0                                 # num_seqs 0
+    assert lib.pa_decode_append_graph(ctypes.byref(h), *bad) == ops.PA_EINVAL
+    bad = list(args); bad[12] = 96                               # head_dim 96
+    assert lib.pa_decode_append_graph(ctypes.byref(h), *bad) == ops.PA_EUNSUPPORTED
+    bad = list(args); bad[2] = None                              # key
+    assert lib.pa_decode_append_graph(ctypes.byref(h), *bad) == ops.PA_EINVAL
+    assert not h.value
+    assert lib.pa_graph_launch(None, None) == ops.PA_EINVAL
+    assert lib.pa_graph_destroy(None) == ops.PA_OK
 
 
 @pytest.mark.parametrize("kw", [dict(key=None), dict(value=None)])
