@@ -28,8 +28,9 @@
  *             slot_mapping              [num_tokens] int32
  *  Heads      Query head h reads kv head h / (num_q_heads / num_kv_heads):
  *             consecutive query heads share one kv head (grouped-query heads).
- *  Types      dtype applies to q, key, value, caches and out alike.  Attention
- *             accumulates in fp32; out is rounded to nearest even.
+ *  Types      dtype applies to q, key, value, caches and out alike, except
+ *             for an fp8 cache (pa_reshape_and_cache_fp8, pa_decode_fp8).
+ *             Attention accumulates in fp32; out is rounded to nearest even.
  *  Streams    stream is a hipStream_t (NULL = the legacy default stream).  Every
  *             call only enqueues work on it and returns; results are ready when
  *             the stream reaches that point.  Work on one stream runs in call
@@ -59,8 +60,11 @@ extern "C" {
 #endif
 
 typedef enum {
-    PA_F32 = 0,  /* IEEE binary32 */
-    PA_BF16 = 1  /* bfloat16 */
+    PA_F32 = 0,      /* IEEE binary32 */
+    PA_BF16 = 1,     /* bfloat16 */
+    PA_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("E4M3FN": bias 7, max 448, no infinities);
+                        storage of an fp8 cache only: accepted by the bit copies
+                        pa_reshape_and_cache and pa_copy_blocks */
 } pa_dtype;
 
 typedef enum {
@@ -85,6 +89,29 @@ int pa_reshape_and_cache(const void *key, const void *value,
                          const int32_t *slot_mapping, int32_t num_tokens,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int64_t num_blocks, pa_dtype dtype, void *stream);
+
+/*
+ * FP8 KV cache.  The pages name quantized inference as a later topic (page
+ * "从零实现一个 mini vLLM--开篇", section "5. 这个系列会怎么展开", stage six,
+ * and section "6. 我们不会一开始就做什么") without fixing a format; here a
+ * cache may hold OCP FP8 E4M3 values with one scale per tensor: the value a
+ * stored byte e stands for is k_scale * e4m3(e) in the K cache and
+ * v_scale * e4m3(e) in the V cache.  Same layouts as above, one byte per
+ * element.
+ *
+ * KV append into an fp8 cache: as pa_reshape_and_cache, but every element x
+ * of key (value) is stored as the E4M3 value nearest to
+ * min(max(x * (1/k_scale), -448), 448), ties to even, where 1/k_scale and the
+ * product are IEEE single-precision operations (x read as fp32 from src_dtype
+ * PA_F32 or PA_BF16).  NaN inputs store NaN (0x7F or 0xFF).  k_scale and
+ * v_scale must be finite and > 0 with a finite reciprocal (PA_EINVAL).
+ */
+int pa_reshape_and_cache_fp8(const void *key, const void *value,
+                             void *k_cache, void *v_cache,
+                             const int32_t *slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int64_t num_blocks, pa_dtype src_dtype,
+                             float k_scale, float v_scale, void *stream);
 
 /*
  * Bytes of workspace pa_decode needs for these shapes (0 for invalid head
@@ -158,6 +185,35 @@ int pa_decode_append(void *out, const void *q, const void *key, const void *valu
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode over fp8 caches (written by pa_reshape_and_cache_fp8): what
+ * pa_decode computes with K_t and V_t the dequantized rows k_scale * e4m3(.)
+ * and v_scale * e4m3(.).  q and out are bf16 (dtype must be PA_BF16, else
+ * PA_EUNSUPPORTED).  The kernel forms bf16 products of q and the stored values
+ * (every E4M3 value is exactly a bf16), applies scale * k_scale to the fp32
+ * scores and v_scale to the fp32 output sums.  Same workspace, limits and
+ * errors as pa_decode, plus the scale checks of pa_reshape_and_cache_fp8.
+ */
+int pa_decode_fp8(void *out, const void *q,
+                  const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                  const int32_t *context_lens, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int64_t num_blocks, float scale,
+                  float k_scale, float v_scale, pa_dtype dtype,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* pa_decode_fp8 with the streaming kernel timed, as pa_decode_timed. */
+int pa_decode_fp8_timed(void *out, const void *q,
+                        const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, int32_t max_blocks_per_seq,
+                        const int32_t *context_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int64_t num_blocks, float scale,
+                        float k_scale, float v_scale, pa_dtype dtype,
+                        void *workspace, size_t workspace_bytes, void *stream,
+                        void *kernel_start, void *kernel_stop);
 
 /* pa_decode_append with the streaming kernel timed, as pa_decode_timed. */
 int pa_decode_append_timed(void *out, const void *q, const void *key, const void *value,

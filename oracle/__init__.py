@@ -6,8 +6,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 
 The arithmetic lives in ``pa_oracle.c`` (plain fp64 loops, one token at a
 time through the block table); this module only marshals numpy arrays into
-it.  Element arrays are numpy ``float32`` for fp32 data and ``uint16`` (the raw
-bit patterns) for bfloat16 data.
+it.  Element arrays are numpy ``float32`` for fp32 data, ``uint16`` (the raw
+bit patterns) for bfloat16 data and ``float64`` for values exact only in fp64
+(a dequantized fp8 cache; ``oracle.fp8``).
 
 Every function here is pinned by ``tests/test_oracle.py`` against quantities
 the oracle does not compute itself: dense attention over contiguously laid-out
@@ -31,6 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 DT_F32 = 0
 DT_BF16 = 1
+DT_F64 = 2
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -81,7 +83,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return DT_F32
     if a.dtype == np.uint16:
         return DT_BF16
-    raise TypeError(f"oracle element arrays are float32 or uint16(bf16 bits), got {a.dtype}")
+    if a.dtype == np.float64:
+        return DT_F64
+    raise TypeError(f"oracle element arrays are float32, uint16(bf16 bits) or float64, got {a.dtype}")
 
 
 def _c(a: np.ndarray, dtype=None) -> np.ndarray:

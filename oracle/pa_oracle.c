@@ -28,7 +28,9 @@
  * block table for every single token.  No blocking, no online softmax, no
  * fusion.
  *
- * Element types: 0 = IEEE fp32, 1 = bfloat16 (upper 16 bits of an fp32).
+ * Element types: 0 = IEEE fp32, 1 = bfloat16 (upper 16 bits of an fp32),
+ * 2 = IEEE fp64 (for inputs that are exact only in fp64, such as a dequantized
+ * fp8 cache: scale * e4m3 value).
  * Layouts (all row-major, contiguous):
  *   q, key, value      [rows, heads, head_dim]
  *   k_cache, v_cache   [num_blocks, block_size, num_kv_heads, head_dim]
@@ -43,11 +45,14 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
 
 static double elem_to_double(const void *base, int64_t idx, int dtype) {
     if (dtype == ORACLE_F32) {
         return (double)((const float *)base)[idx];
+    }
+    if (dtype == ORACLE_F64) {
+        return ((const double *)base)[idx];
     }
     /* bfloat16: the 16 stored bits are the high half of an fp32 pattern. */
     uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
@@ -56,7 +61,7 @@ static double elem_to_double(const void *base, int64_t idx, int dtype) {
     return (double)f;
 }
 
-static int elem_bytes(int dtype) { return dtype == ORACLE_F32 ? 4 : 2; }
+static int elem_bytes(int dtype) { return dtype == ORACLE_F32 ? 4 : (dtype == ORACLE_F64 ? 8 : 2); }
 
 /*
  * KV append: for each new token i whose slot is non-negative, its K row and

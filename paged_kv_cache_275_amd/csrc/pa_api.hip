@@ -20,13 +20,25 @@ int check_dtype(pa_dtype dtype) {
     return (dtype == PA_F32 || dtype == PA_BF16) ? PA_OK : PA_EUNSUPPORTED;
 }
 
-int elem_bytes(pa_dtype dtype) { return dtype == PA_F32 ? 4 : 2; }
+// Element types of a cache for the bit copies (fp8 caches included).
+int check_storage_dtype(pa_dtype dtype) {
+    return (dtype == PA_F32 || dtype == PA_BF16 || dtype == PA_FP8_E4M3) ? PA_OK : PA_EUNSUPPORTED;
+}
+
+int elem_bytes(pa_dtype dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
 
 int check_cache_shape(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks) {
     if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0) return PA_EINVAL;
     if (num_blocks > INT32_MAX / block_size) return PA_EINVAL;  // slots must fit int32
     if (block_size != 16) return PA_EUNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return PA_EUNSUPPORTED;
+    return PA_OK;
+}
+
+// FP8 cache scales: finite, positive, and with a finite reciprocal.
+int check_kv_scales(float k_scale, float v_scale) {
+    const float lo = 1.0f / 3.0e38f;
+    if (!(isfinite(k_scale) && isfinite(v_scale) && k_scale > lo && v_scale > lo)) return PA_EINVAL;
     return PA_OK;
 }
 
@@ -116,7 +128,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
                          void* stream) {
-    int rc = check_dtype(dtype);
+    int rc = check_storage_dtype(dtype);
     if (rc) return rc;
     if (num_tokens < 0) return PA_EINVAL;
     rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
@@ -130,9 +142,32 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype src_dtype,
+                             float k_scale, float v_scale, void* stream) {
+    int rc = check_dtype(src_dtype);
+    if (rc) return rc;
+    if (num_tokens < 0) return PA_EINVAL;
+    rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
+    if (rc) return rc;
+    rc = check_kv_scales(k_scale, v_scale);
+    if (rc) return rc;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_EINVAL;
+    const long long row_elems = (long long)num_kv_heads * head_dim;
+    if (row_elems * 4 > INT32_MAX) return PA_EUNSUPPORTED;
+    // the reciprocals, in IEEE single precision, are what multiplies the inputs
+    const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+    hipError_t e = pa::launch_reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                                    (int)row_elems, src_dtype == PA_BF16, k_inv, v_inv,
+                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
                    int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
-    int rc = check_dtype(dtype);
+    int rc = check_storage_dtype(dtype);
     if (rc) return rc;
     if (num_pairs < 0) return PA_EINVAL;
     rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
@@ -158,16 +193,27 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 namespace {
 
-// pa_decode and its fused-append and timed variants: key/value non-null means
-// fused append (the caches are then written).
+// Scales of an FP8 E4M3 cache (dequantized value = scale * stored value).
+struct KvScales {
+    float k, v;
+};
+
+// pa_decode and its fused-append, fp8-cache and timed variants: key/value
+// non-null means fused append (the caches are then written); kv8 non-null
+// means the caches hold FP8 E4M3 (q and out bf16).
 int decode_impl(void* out, const void* q, const void* key, const void* value, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                 int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
                 void* workspace, size_t workspace_bytes, void* stream, void* kernel_start, void* kernel_stop,
-                bool fused, bool launch = true) {
+                bool fused, bool launch = true, const KvScales* kv8 = nullptr) {
     int rc = check_dtype(dtype);
     if (rc) return rc;
+    if (kv8) {
+        if (dtype != PA_BF16 || fused) return PA_EUNSUPPORTED;
+        rc = check_kv_scales(kv8->k, kv8->v);
+        if (rc) return rc;
+    }
     if (num_seqs < 0) return PA_EINVAL;
     rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
     if (rc) return rc;
@@ -214,10 +260,12 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     // PA_DECODE_SWITCH_TICKS (0..64) overrides the segment cost, for sweeps
     a.unit_ticks = pa::kDecodeUnitTicks;
     a.switch_ticks = std::min(64, env_int("PA_DECODE_SWITCH_TICKS", pa::kDecodeSwitchTicks, 0));
-    a.scale_log2 = scale * 1.4426950408889634f;
+    a.scale_log2 = (kv8 ? scale * kv8->k : scale) * 1.4426950408889634f;
+    a.v_scale = kv8 ? kv8->v : 1.0f;
     // PA_DECODE_STAGES (2, 3 or 4) selects the pipeline depth, for sweeps
     const int stages = env_int("PA_DECODE_STAGES", pa::kDecodeStages);
-    hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, static_cast<hipStream_t>(stream),
+    hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, kv8 != nullptr,
+                                     static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(kernel_start), static_cast<hipEvent_t>(kernel_stop));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
@@ -242,6 +290,29 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
     return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                        workspace, workspace_bytes, stream, kernel_start, kernel_stop, false);
+}
+
+int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                  float k_scale, float v_scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    const KvScales kv{k_scale, v_scale};
+    return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                       workspace, workspace_bytes, stream, nullptr, nullptr, false, true, &kv);
+}
+
+int pa_decode_fp8_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int64_t num_blocks, float scale, float k_scale, float v_scale,
+                        pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream, void* kernel_start,
+                        void* kernel_stop) {
+    const KvScales kv{k_scale, v_scale};
+    return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                       workspace, workspace_bytes, stream, kernel_start, kernel_stop, false, true, &kv);
 }
 
 int pa_decode_append(void* out, const void* q, const void* key, const void* value, void* k_cache,

@@ -58,6 +58,8 @@
 //    tokens get zero rows.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -142,6 +144,36 @@ __device__ __forceinline__ void pv_block_packed(float (&acc)[GP][KDPL], float (&
                 acc[g][c * 8 + 2 * j] = dot2_bf16(ev, pk[g], acc[g][c * 8 + 2 * j]);
                 acc[g][c * 8 + 2 * j + 1] = dot2_bf16(od, pk[g], acc[g][c * 8 + 2 * j + 1]);
             }
+        }
+    }
+}
+
+// FP8 E4M3 V: as pv_block_packed, from the raw bytes of the lane's KDPL
+// contiguous dims of tokens 0 and 1 (vr[t][0]; KDPL = 8 uses .x and .y).  The
+// bytes of the two tokens are interleaved by v_perm, converted in pairs
+// (exactly) to fp32, then packed to bf16 pairs for v_dot2.
+template <int GP, int KDPL>
+__device__ __forceinline__ void pv_block_fp8(float (&acc)[GP][KDPL], float (&l)[GP], const uint32_t (&pk)[GP],
+                                             const uint4 (&vr)[2][1]) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g) l[g] = dot2_bf16(pk[g], 0x3F803F80u, l[g]);
+    const uint32_t v0[4] = {vr[0][0].x, vr[0][0].y, vr[0][0].z, vr[0][0].w};
+    const uint32_t v1[4] = {vr[1][0].x, vr[1][0].y, vr[1][0].z, vr[1][0].w};
+#pragma unroll
+    for (int w = 0; w < KDPL / 4; ++w) {
+        // (t0 d, t1 d, t0 d+1, t1 d+1) and the same for d+2, d+3
+        const uint32_t lo = __builtin_amdgcn_perm(v1[w], v0[w], 0x05010400u);
+        const uint32_t hi = __builtin_amdgcn_perm(v1[w], v0[w], 0x07030602u);
+        const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+        const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+        const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+        const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+        const uint32_t pr[4] = {pack_bf16x2(f0.x, f0.y), pack_bf16x2(f1.x, f1.y), pack_bf16x2(f2.x, f2.y),
+                                pack_bf16x2(f3.x, f3.y)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int g = 0; g < GP; ++g) acc[g][4 * w + i] = dot2_bf16(pr[i], pk[g], acc[g][4 * w + i]);
         }
     }
 }
@@ -388,13 +420,21 @@ __device__ __forceinline__ int block_at_tick(long long t, long long T, const int
     return pref[s] + min((r + R - 1) / R, nb);
 }
 
-template <typename T, int D, int GP, int NW, int STAGES, int WIN>
+// KV8: the caches hold FP8 E4M3 (q and out stay T = bf16); dequantized values
+// are k_scale * e4m3 and v_scale * e4m3, k_scale folded into scale_log2 and
+// v_scale applied when a segment closes.  A lane then holds kDpl CONTIGUOUS
+// dims of V (one chunk of kE = kDpl bytes), and for scores lane group g loads
+// the 16 bytes at dims 64p + 16g of a key, which feed MFMA steps 2p and 2p+1
+// (the query rows are loaded with the same dim order).
+template <typename T, int D, int GP, int NW, int STAGES, int WIN, bool KV8>
 __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a) {
     using G = DecodeGeom<T, D>;
+    using KVT = typename std::conditional<KV8, uint8_t, T>::type;  // cache element
+    static_assert(!KV8 || sizeof(T) == 2, "an fp8 cache goes with bf16 queries");
     constexpr int kDpl = G::kDpl;
-    constexpr int kVecs = G::kVecs;
+    constexpr int kVecs = KV8 ? 1 : G::kVecs;
     constexpr int kQb = G::kQb;
-    constexpr int kE = G::kE;
+    constexpr int kE = KV8 ? kDpl : G::kE;
 
     extern __shared__ int smem[];
     __shared__ int2 scan_scratch[NW];
@@ -423,7 +463,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             }
         }
     }
-    if (a.new_k != nullptr && threadIdx.x < kWave) {
+    if (!KV8 && a.new_k != nullptr && threadIdx.x < kWave) {
         // Fused KV append: wave 0 of each workgroup copies the new token's K/V
         // rows of some sequences into their cache slots (position N-1).  No
         // wave of this kernel reads those slots: the units holding a new token
@@ -476,8 +516,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     const int hkv_heads = a.num_kv_heads;
     const uint32_t lane_off = ((uint32_t)tg * hkv_heads) * D + dl * kE;
     const uint32_t tok8_off = 8u * hkv_heads * D;
-    const T* kbase = reinterpret_cast<const T*>(a.k_cache);
-    const T* vbase = reinterpret_cast<const T*>(a.v_cache);
+    const KVT* kbase = reinterpret_cast<const KVT*>(a.k_cache);
+    const KVT* vbase = reinterpret_cast<const KVT*>(a.v_cache);
 
     // consume-side position: sequence, block, blocks in sequence
     int cs = find_seq(pref, S, 1, u_begin);
@@ -493,7 +533,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     constexpr int kRows = (GP + 3) / 4;  // 16-lane row groups that hold heads
     const int mrow = lane >> 4;
     const int mtok = lane & 15;
-    const uint32_t kmf_off = ((uint32_t)mtok * hkv_heads) * D + 8 * mrow;
+    const uint32_t kmf_off = ((uint32_t)mtok * hkv_heads) * D + (KV8 ? 16 : 8) * mrow;
     uint32_t* lp = reinterpret_cast<uint32_t*>(tabs + NW * WIN) + (wv % NW) * (4 * 8 * 4);
 
     // Staging of finished segments.  A global store holds up the completion
@@ -572,34 +612,42 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         // changes addresses only, never the number of loads
         const uint32_t nrow = __builtin_amdgcn_readfirstlane(e.w);
         const int noff = vld[st] - 1;  // the new token is the block's last valid one
-        const T* vb0 = vbase + base + lane_off;
-        const T* vb1 = vb0 + tok8_off;
-        const T* kt0 = kbase + base + lane_off;
-        const T* kt1 = kt0 + tok8_off;
-        if (nrow != 0xFFFFFFFFu) {
+        const KVT* vb0 = vbase + base + lane_off;
+        const KVT* vb1 = vb0 + tok8_off;
+        const KVT* kt0 = kbase + base + lane_off;
+        const KVT* kt1 = kt0 + tok8_off;
+        if (!KV8 && nrow != 0xFFFFFFFFu) {
             const size_t in_off = (size_t)nrow * D + dl * kE;
             if (tg == noff) {
-                vb0 = reinterpret_cast<const T*>(a.new_v) + in_off;
-                kt0 = reinterpret_cast<const T*>(a.new_k) + in_off;
+                vb0 = reinterpret_cast<const KVT*>(a.new_v) + in_off;
+                kt0 = reinterpret_cast<const KVT*>(a.new_k) + in_off;
             }
             if (tg + 8 == noff) {
-                vb1 = reinterpret_cast<const T*>(a.new_v) + in_off;
-                kt1 = reinterpret_cast<const T*>(a.new_k) + in_off;
+                vb1 = reinterpret_cast<const KVT*>(a.new_v) + in_off;
+                kt1 = reinterpret_cast<const KVT*>(a.new_k) + in_off;
             }
         }
         if constexpr (kMfma) {
-            const T* kb = kbase + base + kmf_off;
-            if (nrow != 0xFFFFFFFFu && mtok == noff)
-                kb = reinterpret_cast<const T*>(a.new_k) + (size_t)nrow * D + 8 * mrow;
+            const KVT* kb = kbase + base + kmf_off;
+            if (!KV8 && nrow != 0xFFFFFFFFu && mtok == noff)
+                kb = reinterpret_cast<const KVT*>(a.new_k) + (size_t)nrow * D + 8 * mrow;
+            if constexpr (KV8) {
 #pragma unroll
-            for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = *reinterpret_cast<const uint4*>(kb + 32 * mm);
+                for (int p = 0; p < kMf / 2; ++p) kb4[st][p] = *reinterpret_cast<const uint4*>(kb + 64 * p);
+            } else {
+#pragma unroll
+                for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = *reinterpret_cast<const uint4*>(kb + 32 * mm);
+            }
             // the unit's query rows travel with its K/V: no load outside the ring
             // ever has to be waited for (loads complete in issue order)
             const uint32_t qrow0 = __builtin_amdgcn_readfirstlane(e.z);
             const uint32_t hi = mtok < nvh ? (uint32_t)mtok : 0u;
-            const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)(qrow0 + hi) * D + 8 * mrow;
+            const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)(qrow0 + hi) * D;
 #pragma unroll
-            for (int mm = 0; mm < kMf; ++mm) qs[st][mm] = *reinterpret_cast<const uint4*>(qp + 32 * mm);
+            for (int mm = 0; mm < kMf; ++mm) {
+                const int qoff = KV8 ? 64 * (mm / 2) + 16 * mrow + 8 * (mm % 2) : 8 * mrow + 32 * mm;
+                qs[st][mm] = *reinterpret_cast<const uint4*>(qp + qoff);
+            }
         } else {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -610,9 +658,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+            if constexpr (KV8 && kDpl == 8) {  // 8 bytes per lane and token
+                const uint2 v = *reinterpret_cast<const uint2*>(t == 0 ? vb0 : vb1);
+                vr[st][t][0] = make_uint4(v.x, v.y, 0u, 0u);
+            } else {
 #pragma unroll
-            for (int c = 0; c < kVecs; ++c)
-                vr[st][t][c] = *reinterpret_cast<const uint4*>((t == 0 ? vb0 : vb1) + c * 8 * kE);
+                for (int c = 0; c < kVecs; ++c)
+                    vr[st][t][c] = *reinterpret_cast<const uint4*>((t == 0 ? vb0 : vb1) + c * 8 * kE);
+            }
         }
     };
 
@@ -624,6 +677,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         const int slot = first_seg ? 0 : 1;
         float red[kCh];
         reduce_scatter8<GP, kDpl>(red, acc, lane);
+        if constexpr (KV8) {
+#pragma unroll
+            for (int i = 0; i < kCh; ++i) red[i] *= a.v_scale;  // dequantized V = v_scale * e4m3
+        }
         float* sl = stage + nstaged * SG::kWords;
 #pragma unroll
         for (int i = 0; i < kCh; ++i) sl[SG::kMeta + i * kWave + lane] = red[i];
@@ -722,8 +779,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                 if constexpr (kMfma) {
                     // ---- scores: S[head][token] = Q K^T on the matrix cores
                     f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (KV8) {
 #pragma unroll
-                    for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qs[st][mm], kb4[st][mm], s4);
+                        for (int p = 0; p < kMf / 2; ++p) {
+                            const uint4 r = kb4[st][p];
+                            s4 = mfma16x16x32_bf16(qs[st][2 * p], fp8x8_to_bf16x8(r.x, r.y), s4);
+                            s4 = mfma16x16x32_bf16(qs[st][2 * p + 1], fp8x8_to_bf16x8(r.z, r.w), s4);
+                        }
+                    } else {
+#pragma unroll
+                        for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qs[st][mm], kb4[st][mm], s4);
+                    }
                     float sv[4];
                     bool need = false;
 #pragma unroll
@@ -776,7 +842,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                             if (4 * rg + r < GP) pk[4 * rg + r] = vv[r];
                         }
                     }
-                    pv_block_packed<GP, kDpl, kVecs>(acc, l, pk, vr[st]);
+                    if constexpr (KV8) {
+                        pv_block_fp8<GP, kDpl>(acc, l, pk, vr[st]);
+                    } else {
+                        pv_block_packed<GP, kDpl, kVecs>(acc, l, pk, vr[st]);
+                    }
                 } else {
                     // ---- scores of this block
                     float sc[2][GP];
@@ -931,11 +1001,11 @@ static size_t decode_stream_lds_bytes(int num_seqs) {
 
 // Events, when given, take the kernel's own start and stop times from its
 // dispatch (hipExtLaunchKernel): no extra packets on the stream.
-template <typename T, int D, int GP, int STAGES>
+template <typename T, int D, int GP, int STAGES, bool KV8>
 static hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const size_t lds = decode_stream_lds_bytes<GP, D>(a.num_seqs);
     const dim3 grid((a.waves + kDecodeWaves - 1) / kDecodeWaves), block(kDecodeWaves * kWave);
-    auto kernel = decode_stream_kernel<T, D, GP, kDecodeWaves, STAGES, kDecodeWindow>;
+    auto kernel = decode_stream_kernel<T, D, GP, kDecodeWaves, STAGES, kDecodeWindow, KV8>;
     if (ev_start || ev_stop) {
         DecodeArgs arg = a;
         void* args[] = {&arg};
@@ -947,13 +1017,21 @@ static hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream, hipEven
 }
 
 template <typename T, int D, int GP>
-static hipError_t launch_decode_g(const DecodeArgs& a, int stages, hipStream_t stream, hipEvent_t ev_start,
+static hipError_t launch_decode_g(const DecodeArgs& a, int stages, bool kv8, hipStream_t stream, hipEvent_t ev_start,
                                   hipEvent_t ev_stop) {
     hipError_t e;
-    switch (stages) {
-        case 2: e = launch_stream<T, D, GP, 2>(a, stream, ev_start, ev_stop); break;
-        case 3: e = launch_stream<T, D, GP, 3>(a, stream, ev_start, ev_stop); break;
-        default: e = launch_stream<T, D, GP, 4>(a, stream, ev_start, ev_stop); break;
+    if (kv8) {
+        if constexpr (sizeof(T) == 2) {
+            e = launch_stream<T, D, GP, kDecodeStages, true>(a, stream, ev_start, ev_stop);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else {
+        switch (stages) {
+            case 2: e = launch_stream<T, D, GP, 2, false>(a, stream, ev_start, ev_stop); break;
+            case 3: e = launch_stream<T, D, GP, 3, false>(a, stream, ev_start, ev_stop); break;
+            default: e = launch_stream<T, D, GP, 4, false>(a, stream, ev_start, ev_stop); break;
+        }
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_fixup_kernel<T, D, GP>), dim3(a.waves), dim3(GP * kWave), 0, stream, a);
@@ -961,24 +1039,25 @@ static hipError_t launch_decode_g(const DecodeArgs& a, int stages, hipStream_t s
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int stages, hipStream_t stream, hipEvent_t e0,
-                                  hipEvent_t e1) {
+static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int stages, bool kv8, hipStream_t stream,
+                                  hipEvent_t e0, hipEvent_t e1) {
     switch (gp) {
-        case 1: return launch_decode_g<T, D, 1>(a, stages, stream, e0, e1);
-        case 2: return launch_decode_g<T, D, 2>(a, stages, stream, e0, e1);
-        case 4: return launch_decode_g<T, D, 4>(a, stages, stream, e0, e1);
-        default: return launch_decode_g<T, D, 8>(a, stages, stream, e0, e1);
+        case 1: return launch_decode_g<T, D, 1>(a, stages, kv8, stream, e0, e1);
+        case 2: return launch_decode_g<T, D, 2>(a, stages, kv8, stream, e0, e1);
+        case 4: return launch_decode_g<T, D, 4>(a, stages, kv8, stream, e0, e1);
+        default: return launch_decode_g<T, D, 8>(a, stages, kv8, stream, e0, e1);
     }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages,
+hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages, bool kv8,
                          hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     if (dtype_bf16) {
-        return head_dim == 64 ? launch_decode_d<uint16_t, 64>(a, gp, stages, stream, e0, e1)
-                              : launch_decode_d<uint16_t, 128>(a, gp, stages, stream, e0, e1);
+        return head_dim == 64 ? launch_decode_d<uint16_t, 64>(a, gp, stages, kv8, stream, e0, e1)
+                              : launch_decode_d<uint16_t, 128>(a, gp, stages, kv8, stream, e0, e1);
     }
-    return head_dim == 64 ? launch_decode_d<float, 64>(a, gp, stages, stream, e0, e1)
-                          : launch_decode_d<float, 128>(a, gp, stages, stream, e0, e1);
+    if (kv8) return hipErrorInvalidValue;
+    return head_dim == 64 ? launch_decode_d<float, 64>(a, gp, stages, false, stream, e0, e1)
+                          : launch_decode_d<float, 128>(a, gp, stages, false, stream, e0, e1);
 }
 
 }  // namespace pa

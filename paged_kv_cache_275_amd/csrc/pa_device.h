@@ -108,4 +108,30 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- FP8 E4M3 (OCP "E4M3FN": bias 7, largest finite 448, no infinities).
+// gfx950's conversions use this format and round to nearest even; a value
+// beyond +-448 would become NaN, so quantization clamps first.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+constexpr float kFp8Max = 448.0f;
+
+// Eight fp8 values (two dwords, value 0 in the low byte) as eight bf16, in
+// order, in a uint4 (an MFMA operand).  Exact: every e4m3 value is a bf16.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(c.x, c.y), pack_bf16x2(d.x, d.y));
+}
+
+// Clamp to the finite range, NaN kept (comparisons with NaN are false).
+__device__ __forceinline__ float fp8_clamp(float x) { return x > kFp8Max ? kFp8Max : (x < -kFp8Max ? -kFp8Max : x); }
+
+// Four floats to four e4m3 bytes (value 0 in the low byte), nearest even.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(c), fp8_clamp(d), w, true);
+    return (uint32_t)w;
+}
+
 }  // namespace pa

@@ -62,7 +62,8 @@ struct DecodeArgs {
     int wave_groups;    // groups of n_kvg waves; group g streams the g-th share of all blocks
     int unit_ticks;     // work-split cost of one unit (one block of one head group)
     int switch_ticks;   // extra cost of closing a segment (one head group of a sequence)
-    float scale_log2;   // scale * log2(e)
+    float scale_log2;   // scale * log2(e) (times k_scale for an fp8 cache)
+    float v_scale;      // fp8 cache: dequantized V = v_scale * stored value (unused otherwise)
 };
 
 struct PrefillArgs {
@@ -86,13 +87,17 @@ constexpr int kPrefillMaxGroup = 16;
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, hipStream_t stream);
 // Launches the streaming kernel and the split-segment merge.  Non-null events
-// receive the streaming kernel's start and stop times.
-hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages,
+// receive the streaming kernel's start and stop times.  kv8: the caches hold
+// FP8 E4M3 (bf16 queries only; the default stage count is used).
+hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages, bool kv8,
                          hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int num_tokens, int row_bytes,
                                     hipStream_t stream);
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                                        const int32_t* slot_mapping, int num_tokens, int row_elems, bool src_bf16,
+                                        float k_inv, float v_inv, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int block_bytes,
                               hipStream_t stream);
 

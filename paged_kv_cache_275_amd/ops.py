@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "pa.h")
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_ELAUNCH, PA_ENOMEM = 0, -1, -2, -3, -4, -5
 BLOCK_SIZE = 16
 
@@ -43,6 +44,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                             ctypes.c_size_t)
     lib.pa_reshape_and_cache.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i64, ctypes.c_int, p]
     lib.pa_reshape_and_cache.restype = ctypes.c_int
+    lib.pa_reshape_and_cache_fp8.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i64, ctypes.c_int, f32, f32, p]
+    lib.pa_reshape_and_cache_fp8.restype = ctypes.c_int
+    lib.pa_decode_fp8.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32, f32, f32,
+                                  ctypes.c_int, p, sz, p]
+    lib.pa_decode_fp8.restype = ctypes.c_int
+    lib.pa_decode_fp8_timed.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32, f32, f32,
+                                        ctypes.c_int, p, sz, p, p, p]
+    lib.pa_decode_fp8_timed.restype = ctypes.c_int
     lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_workspace_size.restype = sz
     lib.pa_decode.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
@@ -94,7 +103,9 @@ def _dtype_code(t) -> int:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError(f"unsupported element type {t.dtype}; use float32 or bfloat16")
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):  # the bytes of an fp8 cache
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported element type {t.dtype}; use float32, bfloat16 or fp8 (uint8) bytes")
 
 
 def _need(t, name: str, dtype=None, dim: Optional[int] = None):
@@ -152,6 +163,40 @@ def bind_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=No
     def call():
         _check(lib, "pa_reshape_and_cache", fn(*args))
     return call
+
+
+def _need_fp8_cache(t, name: str):
+    import torch
+    _need(t, name, dim=4)
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must hold fp8 E4M3 bytes (torch.uint8 or torch.float8_e4m3fn), got {t.dtype}")
+
+
+def _reshape_and_cache_fp8_args(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream) -> tuple:
+    import torch
+    _need(key, "key", dim=3)
+    _need(value, "value", key.dtype, 3)
+    _need_fp8_cache(k_cache, "k_cache")
+    _need_fp8_cache(v_cache, "v_cache")
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    nb, bs, hkv, d = k_cache.shape
+    if tuple(key.shape[1:]) != (hkv, d) or value.shape != key.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("key/value [T, Hkv, D] must match caches [NB, 16, Hkv, D]")
+    if slot_mapping.shape[0] != key.shape[0]:
+        raise ValueError("slot_mapping must have one entry per token")
+    return (key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            slot_mapping.data_ptr(), key.shape[0], hkv, d, bs, nb, _dtype_code(key), float(k_scale),
+            float(v_scale), _stream_handle(key, stream))
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale: float, v_scale: float,
+                          stream=None) -> None:
+    """KV append into fp8 caches (pa_reshape_and_cache_fp8): key/value fp32 or
+    bf16 [T, Hkv, D]; caches uint8 [NB, 16, Hkv, D] holding E4M3 bytes, whose
+    values are k_scale (v_scale) times the stored number."""
+    lib = load_library()
+    args = _reshape_and_cache_fp8_args(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream)
+    _check(lib, "pa_reshape_and_cache_fp8", lib.pa_reshape_and_cache_fp8(*args))
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
@@ -227,6 +272,60 @@ def bind_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: flo
             _check(lib, "pa_decode", plain(*args))
         else:
             _check(lib, "pa_decode_timed", timed(*args, *kernel_events))
+    return call
+
+
+def _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale, workspace,
+                     stream) -> tuple:
+    import torch
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", q.dtype, 3)
+    _need_fp8_cache(k_cache, "k_cache")
+    _need_fp8_cache(v_cache, "v_cache")
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    s, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    if out.shape != q.shape or dk != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q/out and the caches")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    if workspace is None:
+        workspace = decode_workspace(q, k_cache, block_tables)
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), s,
+            hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale), PA_BF16, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(q, stream))
+    return args, workspace
+
+
+def decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, k_scale: float,
+               v_scale: float, workspace=None, stream=None, kernel_events=None) -> None:
+    """Paged-attention decode over fp8 caches (pa_decode_fp8): q/out bf16
+    [S, Hq, D], caches uint8 E4M3 bytes; kernel_events as in decode()."""
+    lib = load_library()
+    args, _ = _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                               workspace, stream)
+    if kernel_events is None:
+        _check(lib, "pa_decode_fp8", lib.pa_decode_fp8(*args))
+    else:
+        _check(lib, "pa_decode_fp8_timed", lib.pa_decode_fp8_timed(*args, *_event_handles(kernel_events)))
+
+
+def bind_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, k_scale: float,
+                    v_scale: float, workspace=None, stream=None):
+    """Check the arguments once; return f(kernel_events=None) that enqueues the
+    same fp8 decode again (see bind_reshape_and_cache)."""
+    lib = load_library()
+    args, ws = _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                                workspace, stream)
+    plain, timed = lib.pa_decode_fp8, lib.pa_decode_fp8_timed
+
+    def call(kernel_events=None, _keep=ws):
+        if kernel_events is None:
+            _check(lib, "pa_decode_fp8", plain(*args))
+        else:
+            _check(lib, "pa_decode_fp8_timed", timed(*args, *kernel_events))
     return call
 
 
