@@ -83,10 +83,10 @@ int env_int(const char* name, int fallback, int lo = 1) {
     return x >= lo ? x : fallback;
 }
 
-// Waves of the persistent decode grid: kDecodeWavesPerCU per compute unit of
+// Waves of the persistent decode grid: per_cu per compute unit of
 // the current device.  PA_DECODE_WAVES overrides the count (launch-shape
 // sweeps and tests); it is read on every call.
-int decode_waves() {
+int decode_waves(int per_cu) {
     static int cached_cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -97,7 +97,7 @@ int decode_waves() {
             cus = 256;
         cached_cus[slot] = cus;
     }
-    long long w = (long long)cus * pa::kDecodeWavesPerCU;
+    long long w = (long long)cus * per_cu;
     if (const char* env = getenv("PA_DECODE_WAVES")) {
         const long long e = atoll(env);
         if (e > 0) w = e;
@@ -254,7 +254,10 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.n_kvg = num_kv_heads * a.groups_per_kv;
     // wave groups of n_kvg waves (one per head group), as many as fit the
     // persistent grid and the workspace records
-    a.wave_groups = std::max(1, std::min(decode_waves(), pa::kDecodeMaxWaves) / a.n_kvg);
+    const bool two_groups_fit = (head_dim == 64 || gp <= 4) &&
+                                2 * pa::decode_lds_bytes(head_dim, gp, num_seqs) <= pa::kLdsBytesPerCU;
+    const int per_cu = kv8 && two_groups_fit ? pa::kDecodeWavesPerCUFp8 : pa::kDecodeWavesPerCU;
+    a.wave_groups = std::max(1, std::min(decode_waves(per_cu), pa::kDecodeMaxWaves) / a.n_kvg);
     if ((long long)a.wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
     a.waves = a.wave_groups * a.n_kvg;
     // PA_DECODE_SWITCH_TICKS (0..64) overrides the segment cost, for sweeps
@@ -262,8 +265,10 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.switch_ticks = std::min(64, env_int("PA_DECODE_SWITCH_TICKS", pa::kDecodeSwitchTicks, 0));
     a.scale_log2 = (kv8 ? scale * kv8->k : scale) * 1.4426950408889634f;
     a.v_scale = kv8 ? kv8->v : 1.0f;
-    // PA_DECODE_STAGES (2, 3 or 4) selects the pipeline depth, for sweeps
-    const int stages = env_int("PA_DECODE_STAGES", pa::kDecodeStages);
+    // PA_DECODE_STAGES (2, 3 or 4; fp8 caches also 6 or 8) selects the
+    // pipeline depth, for sweeps
+    const int stages = env_int("PA_DECODE_STAGES", per_cu == pa::kDecodeWavesPerCUFp8 ? pa::kDecodeStagesFp8Pair
+                                                                                        : pa::kDecodeStages);
     hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, kv8 != nullptr,
                                      static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(kernel_start), static_cast<hipEvent_t>(kernel_stop));

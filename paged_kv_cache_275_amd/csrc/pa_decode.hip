@@ -150,8 +150,8 @@ __device__ __forceinline__ void pv_block_packed(float (&acc)[GP][KDPL], float (&
 
 // FP8 E4M3 V: as pv_block_packed, from the raw bytes of the lane's KDPL
 // contiguous dims of tokens 0 and 1 (vr[t][0]; KDPL = 8 uses .x and .y).  The
-// bytes of the two tokens are interleaved by v_perm, converted in pairs
-// (exactly) to fp32, then packed to bf16 pairs for v_dot2.
+// bytes of the two tokens are interleaved by v_perm and converted in pairs
+// (exactly) to the bf16 pairs v_dot2 takes.
 template <int GP, int KDPL>
 __device__ __forceinline__ void pv_block_fp8(float (&acc)[GP][KDPL], float (&l)[GP], const uint32_t (&pk)[GP],
                                              const uint4 (&vr)[2][1]) {
@@ -164,12 +164,8 @@ __device__ __forceinline__ void pv_block_fp8(float (&acc)[GP][KDPL], float (&l)[
         // (t0 d, t1 d, t0 d+1, t1 d+1) and the same for d+2, d+3
         const uint32_t lo = __builtin_amdgcn_perm(v1[w], v0[w], 0x05010400u);
         const uint32_t hi = __builtin_amdgcn_perm(v1[w], v0[w], 0x07030602u);
-        const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-        const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-        const f32x2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-        const f32x2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-        const uint32_t pr[4] = {pack_bf16x2(f0.x, f0.y), pack_bf16x2(f1.x, f1.y), pack_bf16x2(f2.x, f2.y),
-                                pack_bf16x2(f3.x, f3.y)};
+        const uint32_t pr[4] = {fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
+                                fp8x2_to_bf16x2<true>(hi)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -1022,7 +1018,13 @@ static hipError_t launch_decode_g(const DecodeArgs& a, int stages, bool kv8, hip
     hipError_t e;
     if (kv8) {
         if constexpr (sizeof(T) == 2) {
-            e = launch_stream<T, D, GP, kDecodeStages, true>(a, stream, ev_start, ev_stop);
+            switch (stages) {
+                case 2: e = launch_stream<T, D, GP, 2, true>(a, stream, ev_start, ev_stop); break;
+                case 3: e = launch_stream<T, D, GP, 3, true>(a, stream, ev_start, ev_stop); break;
+                case 6: e = launch_stream<T, D, GP, 6, true>(a, stream, ev_start, ev_stop); break;
+                case 8: e = launch_stream<T, D, GP, 8, true>(a, stream, ev_start, ev_stop); break;
+                default: e = launch_stream<T, D, GP, 4, true>(a, stream, ev_start, ev_stop); break;
+            }
         } else {
             return hipErrorInvalidValue;
         }
@@ -1046,6 +1048,23 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int stages, bool 
         case 2: return launch_decode_g<T, D, 2>(a, stages, kv8, stream, e0, e1);
         case 4: return launch_decode_g<T, D, 4>(a, stages, kv8, stream, e0, e1);
         default: return launch_decode_g<T, D, 8>(a, stages, kv8, stream, e0, e1);
+    }
+}
+
+size_t decode_lds_bytes(int head_dim, int gp, int num_seqs) {
+    if (head_dim == 64) {
+        switch (gp) {
+            case 1: return decode_stream_lds_bytes<1, 64>(num_seqs);
+            case 2: return decode_stream_lds_bytes<2, 64>(num_seqs);
+            case 4: return decode_stream_lds_bytes<4, 64>(num_seqs);
+            default: return decode_stream_lds_bytes<8, 64>(num_seqs);
+        }
+    }
+    switch (gp) {
+        case 1: return decode_stream_lds_bytes<1, 128>(num_seqs);
+        case 2: return decode_stream_lds_bytes<2, 128>(num_seqs);
+        case 4: return decode_stream_lds_bytes<4, 128>(num_seqs);
+        default: return decode_stream_lds_bytes<8, 128>(num_seqs);
     }
 }
 

@@ -111,17 +111,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---- FP8 E4M3 (OCP "E4M3FN": bias 7, largest finite 448, no infinities).
 // gfx950's conversions use this format and round to nearest even; a value
 // beyond +-448 would become NaN, so quantization clamps first.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kFp8Max = 448.0f;
 
+// Two fp8 values (bytes 0 and 1 of w, or bytes 2 and 3 when HI) as a bf16
+// pair, first value in the low half.  Exact: every e4m3 value is a bf16.  The
+// gfx950 conversion takes an f32 scale of which it uses only the exponent;
+// 1.0 leaves the values as they are.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // Eight fp8 values (two dwords, value 0 in the low byte) as eight bf16, in
-// order, in a uint4 (an MFMA operand).  Exact: every e4m3 value is a bf16.
+// order, in a uint4 (an MFMA operand).
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-    return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(c.x, c.y), pack_bf16x2(d.x, d.y));
+    return make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                      fp8x2_to_bf16x2<true>(w1));
 }
 
 // Clamp to the finite range, NaN kept (comparisons with NaN are false).

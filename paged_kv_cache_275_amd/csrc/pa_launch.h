@@ -11,9 +11,16 @@ namespace pa {
 // block) units with kDecodeStages blocks in flight; block ids are staged in
 // LDS kDecodeWindow units at a time.
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeStages = 4;      // default; 2 and 3 are also built
+constexpr int kDecodeStages = 4;      // default; 2 and 3 are also built (fp8 caches: 2, 3, 6, 8)
 constexpr int kDecodeWindow = 256;
 constexpr int kDecodeWavesPerCU = 4;
+// An fp8 cache halves the bytes per unit but not the instructions: with two
+// waves per SIMD one wave's arithmetic covers the other's waits.  Used when
+// two workgroups fit a compute unit (registers: head_dim 64 or at most 4 heads
+// per wave; LDS: see decode_lds_bytes).
+constexpr int kDecodeWavesPerCUFp8 = 8;
+constexpr int kDecodeStagesFp8Pair = 2;  // blocks in flight per wave when two waves share a SIMD
+constexpr size_t kLdsBytesPerCU = 160 * 1024;
 constexpr int kDecodeMaxWaves = 4096;   // workspace records are sized for this many waves
 constexpr int kDecodeMaxSeqs = 8192;    // sequence prefix sums live in LDS
 // Work-split costs: closing a segment takes about as long as streaming one
@@ -88,7 +95,9 @@ constexpr int kPrefillMaxGroup = 16;
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, hipStream_t stream);
 // Launches the streaming kernel and the split-segment merge.  Non-null events
 // receive the streaming kernel's start and stop times.  kv8: the caches hold
-// FP8 E4M3 (bf16 queries only; the default stage count is used).
+// FP8 E4M3 (bf16 queries only; 2, 3, 4, 6 or 8 stages).
+// LDS bytes one workgroup of the streaming kernel uses for num_seqs sequences.
+size_t decode_lds_bytes(int head_dim, int gp, int num_seqs);
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages, bool kv8,
                          hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 

@@ -165,10 +165,12 @@ def test_fp8_single_token_returns_scaled_v_exactly(d):
         assert np.array_equal(got[s], np.repeat(v, 4, axis=0)), f"sequence {s}"
 
 
-def test_fp8_unit_scales_match_bf16_decode():
+def test_fp8_unit_scales_match_bf16_decode(monkeypatch):
     """With k_scale = v_scale = 1 the fp8 path and the bf16 path see the same
-    numbers (every E4M3 value is a bf16); they differ only in the order of
-    fp32 sums, so the outputs agree to 2 bf16 units in the last place."""
+    numbers (every E4M3 value is a bf16).  On the same split of the work over
+    waves (the fp8 path otherwise runs twice as many) they differ only in the
+    order of fp32 sums, so the outputs agree to 2 bf16 units in the last place."""
+    monkeypatch.setenv("PA_DECODE_WAVES", "1024")
     rng = np.random.default_rng(77)
     q, kc, vc, bt, lens = _random_fp8_case(rng, 32, 8, 128, [1, 16, 17, 200, 1000, 2500])
     scale = 1.0 / 2048
