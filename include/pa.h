@@ -172,9 +172,11 @@ int pa_decode_timed(void *out, const void *q,
  * to k_cache/v_cache at that position's slot (block_tables[s, (n-1)/16],
  * offset (n-1) % 16), and out is what pa_decode computes over positions
  * 0..n-1, position n-1 included.  The result is that of pa_reshape_and_cache
- * with slot_mapping[s] = that slot, followed by pa_decode, in one kernel
- * launch (plus the split-context merge).  Sequences with n = 0 append nothing
- * and get zero rows.  Same arguments, errors and workspace as pa_decode;
+ * with slot_mapping[s] = that slot, followed by pa_decode, in the two kernel
+ * launches of pa_decode: the attention takes the new rows from key/value, and
+ * the split-context merge that follows also writes them to the cache.
+ * Sequences with n = 0 append nothing and get zero rows.  Same arguments,
+ * errors and workspace as pa_decode;
  * key/value must be non-NULL (PA_EINVAL otherwise) and must not overlap the
  * caches.  Position n-1's slot is overwritten whatever it held.
  */

@@ -459,29 +459,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             }
         }
     }
-    if (!KV8 && a.new_k != nullptr && threadIdx.x < kWave) {
-        // Fused KV append: wave 0 of each workgroup copies the new token's K/V
-        // rows of some sequences into their cache slots (position N-1).  No
-        // wave of this kernel reads those slots: the units holding a new token
-        // take its rows from the inputs instead (see issue below), so the
-        // copies need no ordering against the attention.
-        constexpr int kRowVecsPerHead = D * (int)sizeof(T) / 16;
-        const int row_vecs = a.num_kv_heads * kRowVecsPerHead;
-        for (int sq = blockIdx.x; sq < S; sq += gridDim.x) {
-            const int nq = a.context_lens[sq];
-            if (nq <= 0) continue;
-            const int bq = a.block_tables[(size_t)sq * a.max_blocks_per_seq + (nq - 1) / kBlockTokens];
-            const size_t slot = (size_t)bq * kBlockTokens + (nq - 1) % kBlockTokens;
-            const uint4* ksrc = reinterpret_cast<const uint4*>(a.new_k) + (size_t)sq * row_vecs;
-            const uint4* vsrc = reinterpret_cast<const uint4*>(a.new_v) + (size_t)sq * row_vecs;
-            uint4* kdst = reinterpret_cast<uint4*>(a.k_cache_w) + slot * row_vecs;
-            uint4* vdst = reinterpret_cast<uint4*>(a.v_cache_w) + slot * row_vecs;
-            for (int i = threadIdx.x; i < row_vecs; i += kWave) {
-                kdst[i] = ksrc[i];
-                vdst[i] = vsrc[i];
-            }
-        }
-    }
     const long long NG = a.wave_groups;
     // wave index, made wave-uniform explicitly: everything the wave decides
     // (ranges, segment walk, branches) derives from it, and the compiler would
@@ -918,6 +895,28 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 // the records).
 template <typename T, int D, int GP>
 __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) {
+    if (a.new_k != nullptr) {
+        // Fused KV append: the new token's K/V rows of some sequences go to
+        // their cache slots (position N-1).  The streaming kernel took those
+        // rows from the inputs, so the copies only have to be done by the end
+        // of the call; here they cost the streaming waves nothing.
+        constexpr int kRowVecsPerHead = D * (int)sizeof(T) / 16;
+        const int row_vecs = a.num_kv_heads * kRowVecsPerHead;
+        for (int sq = blockIdx.x; sq < a.num_seqs; sq += gridDim.x) {
+            const int nq = a.context_lens[sq];
+            if (nq <= 0) continue;
+            const int bq = a.block_tables[(size_t)sq * a.max_blocks_per_seq + (nq - 1) / kBlockTokens];
+            const size_t slot = (size_t)bq * kBlockTokens + (nq - 1) % kBlockTokens;
+            const uint4* ksrc = reinterpret_cast<const uint4*>(a.new_k) + (size_t)sq * row_vecs;
+            const uint4* vsrc = reinterpret_cast<const uint4*>(a.new_v) + (size_t)sq * row_vecs;
+            uint4* kdst = reinterpret_cast<uint4*>(a.k_cache_w) + slot * row_vecs;
+            uint4* vdst = reinterpret_cast<uint4*>(a.v_cache_w) + slot * row_vecs;
+            for (int i = threadIdx.x; i < row_vecs; i += blockDim.x) {
+                kdst[i] = ksrc[i];
+                vdst[i] = vsrc[i];
+            }
+        }
+    }
     const int w = blockIdx.x;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
