@@ -234,7 +234,8 @@ def _check_fused(wl, label):
 
 
 @pytest.mark.parametrize("name,num_seqs", [("tiny_fp32", None), ("qwen3_0p6b", 6), ("llama3_8b", 8),
-                                           ("long_skewed", 2), ("mixed_prefill", 6), ("llama3_8b", None)])
+                                           ("long_skewed", 2), ("mixed_prefill", 6), ("llama3_8b", None),
+                                           ("mixed_prefill", None)])
 def test_decode_append_equals_append_then_decode(name, num_seqs):
     """Fused KV append + decode: the whole pool bit for bit as pa_reshape_and_cache
     leaves it, and attention within tolerance of the oracle."""
@@ -289,3 +290,33 @@ def test_decode_append_block_boundaries_and_empty():
     assert np.all(got[7] == 0.0)
     ref = oracle.decode(q, okc, ovc, bt, lens, 0.088)
     assert_attention_close(got, ref, "bf16", "fused boundaries")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (32, 8, 128)])
+def test_decode_append_max_sequences(hq, hkv, d):
+    """8192 sequences in one fused call (more than the merge kernel has
+    workgroups, so each copies the new rows of several), 5% of them empty."""
+    rng = np.random.default_rng(4096 + hq)
+    lens = rng.integers(1, 41, 8192)
+    lens[rng.random(8192) < 0.05] = 0
+    print(f"[gpu] fused max sequences hq={hq} hkv={hkv} d={d} sumN={int(lens.sum())}", flush=True)
+    q, kc, vc, bt, lens = _random_bf16_case(rng, hq, hkv, d, lens.tolist())
+    s = len(lens)
+    key = _bf16_bits(rng, (s, hkv, d))
+    value = _bf16_bits(rng, (s, hkv, d))
+    slots = np.array([int(bt[i, (n - 1) // 16]) * 16 + (n - 1) % 16 if n > 0 else -1
+                      for i, n in enumerate(lens)], np.int32)
+    from tests._gpu import to_dev
+    dkc, dvc = to_dev(kc), to_dev(vc)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / np.sqrt(d)
+    ops.decode_append(out, to_dev(q), to_dev(key), to_dev(value), dkc, dvc, to_dev(bt), to_dev(lens), scale)
+    torch.cuda.synchronize()
+    okc, ovc = kc.copy(), vc.copy()
+    oracle.reshape_and_cache(key, value, okc, ovc, slots)
+    assert to_host(dkc).tobytes() == okc.tobytes()
+    assert to_host(dvc).tobytes() == ovc.tobytes()
+    got = widen_dev(out)
+    assert np.all(got[lens == 0] == 0.0)
+    ref = oracle.decode(q, okc, ovc, bt, lens, scale)
+    assert_attention_close(got, ref, "bf16", f"fused S=8192 hq{hq}/hkv{hkv}/d{d}")
