@@ -464,7 +464,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     // (ranges, segment walk, branches) derives from it, and the compiler would
     // otherwise treat threadIdx-derived values as per-lane and turn the whole
     // control flow into exec-masked vector code
-    const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * NW + threadIdx.x / kWave);
+    // Workgroups are dealt to the 8 XCDs round robin (id mod 8).  Virtual
+    // workgroup ids are numbered so that consecutive ones sit on the same XCD:
+    // the waves of a wave group, which read the kv-head slices of the same
+    // blocks, then go through one L2.
+    const int nwg = (int)gridDim.x;
+    const int vwg = nwg % 8 == 0 ? (int)(blockIdx.x % 8) * (nwg / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(vwg * NW + threadIdx.x / kWave);
     if (wv >= a.waves) return;  // padding waves of the last workgroup (no barrier follows)
     const int lane = threadIdx.x & (kWave - 1);
     const int kvg = wv % n_kvg;                  // this wave's head group
