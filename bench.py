@@ -214,6 +214,43 @@ def graph_step(wl, pools, pre, out, q, kn, vn, bt, cl, ws, stream):
             "graph_step_note": f"pa_decode_append_graph replays over {len(pools)} pool copies, mean of {reps}"}
 
 
+def fp8_prefill(wl, pools, pre, stream):
+    """The chunked prefill over an fp8 copy of the first pool
+    (pa_prefill_chunk_fp8), outside the timed region; mixed workloads only."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_275_amd import ops
+    if pre is None:
+        return {}
+    ks, vs = 0.02, 0.015
+    kc, vc = pools[0]
+    nb, bs, hkv, d = kc.shape
+    slots = torch.arange(nb * bs, dtype=torch.int32, device=kc.device)
+    k8 = torch.empty(kc.shape, dtype=torch.uint8, device=kc.device)
+    v8 = torch.empty_like(k8)
+    ops.reshape_and_cache_fp8(kc.view(-1, hkv, d), vc.view(-1, hkv, d), k8, v8, slots, ks, vs)
+    out8 = torch.empty_like(pre["out"])
+
+    def call():
+        ops.prefill_chunk_fp8(out8, pre["q"], k8, v8, pre["bt"], pre["qsl"], pre["cl"], wl.scale, ks, vs)
+    for _ in range(3):
+        call()
+    reps = 20
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+    flops = prefill_flops(wl)
+    return {"fp8_prefill_us": round(us, 2),
+            "fp8_prefill_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "fp8_prefill_note": f"pa_prefill_chunk_fp8 on the workload's chunks over an fp8 pool copy, mean of {reps}"}
+
+
 def fp8_decode(wl, pools, q, bt, cl, ws, stream):
     """Decode over fp8 E4M3 copies of the pools (pa_decode_fp8), outside the
     timed region.  The copies are quantized on the GPU by
@@ -550,6 +587,7 @@ def main():
         res["extras"].update(graph_step(wl, pools, pre, out, q, k_new[t_new - s_dec:], v_new[t_new - s_dec:], bt, cl,
                                         ws, stream))
     res["extras"].update(fp8_decode(wl, pools, q, bt, cl, ws, stream))
+    res["extras"].update(fp8_prefill(wl, pools, pre, stream))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(res), flush=True)

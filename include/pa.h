@@ -278,6 +278,26 @@ int pa_prefill_chunk(void *out, const void *q,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_prefill_chunk over fp8 caches (written by pa_reshape_and_cache_fp8): the
+ * same causal attention with K_t and V_t the dequantized rows
+ * k_scale * e4m3(.) and v_scale * e4m3(.), so that a chunked-prefill step can
+ * share the fp8 cache with pa_decode_fp8.  q and out are bf16 (dtype must be
+ * PA_BF16).  As in pa_decode_fp8, the stored values are exact bf16 operands,
+ * scale * k_scale applies to the fp32 scores and v_scale to the fp32 output
+ * sums.  Same workspace and errors as pa_prefill_chunk, plus the scale checks
+ * of pa_reshape_and_cache_fp8.
+ */
+int pa_prefill_chunk_fp8(void *out, const void *q,
+                         const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq,
+                         const int32_t *query_start_loc, int32_t total_query_rows,
+                         const int32_t *context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, float scale,
+                         float k_scale, float v_scale, pa_dtype dtype,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Copy on write.  For every pair p < num_pairs, block pairs[2p+1] of k_cache
  * and of v_cache becomes a bit copy of block pairs[2p] (all block_size slots,
  * all heads).  pairs is a DEVICE array [num_pairs, 2] of int32 block ids below

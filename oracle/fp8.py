@@ -18,11 +18,14 @@ tensor, so stored byte e stands for scale * e4m3(e).
 * ``decode_fp8`` -- paged decode attention over the dequantized caches: the
   stored bytes become fp64 values scale * e4m3(e) (exact: a 4-bit significand
   times a 24-bit one) and go through the fp64 decode oracle unchanged.
+* ``prefill_fp8`` -- causal chunked prefill over the dequantized caches, the
+  same way, through the fp64 prefill oracle.
 
 Pins (tests/test_oracle_fp8.py): the value table against PyTorch's
 float8_e4m3fn type and hand-decoded codes, the quantizer against PyTorch's
 cast on clamped inputs, hand-worked ties, the half-spacing error bound and
-monotonicity, and decode_fp8 against dense attention on the dequantized rows.
+monotonicity, and decode_fp8 and prefill_fp8 against dense attention on the
+dequantized rows.
 """
 from __future__ import annotations
 
@@ -128,3 +131,13 @@ def decode_fp8(q_bits, k_codes, v_codes, block_tables, context_lens, scale: floa
     kd = np.ascontiguousarray(dequantize(k_codes, k_scale))
     vd = np.ascontiguousarray(dequantize(v_codes, v_scale))
     return oracle.decode(q64, kd, vd, block_tables, context_lens, scale, seq_range=seq_range)
+
+
+def prefill_fp8(q_bits, k_codes, v_codes, block_tables, query_start_loc, context_lens, scale: float,
+                k_scale: float, v_scale: float, seq_range=None) -> np.ndarray:
+    """fp64 causal chunked prefill over fp8 caches: q as bf16 bits [rows, Hq, D],
+    caches uint8 [nb, 16, Hkv, D]; returns [rows, Hq, D] fp64."""
+    q64 = np.ascontiguousarray(bf16_bits_to_f64(q_bits))
+    kd = np.ascontiguousarray(dequantize(k_codes, k_scale))
+    vd = np.ascontiguousarray(dequantize(v_codes, v_scale))
+    return oracle.prefill(q64, kd, vd, block_tables, query_start_loc, context_lens, scale, seq_range=seq_range)

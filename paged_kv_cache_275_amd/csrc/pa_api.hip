@@ -398,17 +398,20 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t total_query_rows, int
     return 0;
 }
 
-int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                     const int32_t* query_start_loc, int32_t total_query_rows,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                     float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
+namespace {
+
+// pa_prefill_chunk and its fp8-cache variant (kv8 non-null).
+int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                 int32_t max_blocks_per_seq, const int32_t* query_start_loc, int32_t total_query_rows,
+                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                 void* stream, const KvScales* kv8) {
     int rc = check_dtype(dtype);
     if (rc) return rc;
+    if (kv8) {
+        rc = check_kv_scales(kv8->k, kv8->v);
+        if (rc) return rc;
+    }
     if (num_seqs < 0 || total_query_rows < 0) return PA_EINVAL;
     rc = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks);
     if (rc) return rc;
@@ -437,9 +440,42 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.group = group;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    hipError_t e = pa::launch_prefill(a, head_dim, total_query_rows, gp, static_cast<hipStream_t>(stream));
+    a.scale_log2 = (kv8 ? scale * kv8->k : scale) * 1.4426950408889634f;
+    a.v_scale = kv8 ? kv8->v : 1.0f;
+    hipError_t e = pa::launch_prefill(a, head_dim, total_query_rows, gp, kv8 != nullptr,
+                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+}  // namespace
+
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* query_start_loc, int32_t total_query_rows,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                     float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return prefill_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, query_start_loc,
+                        total_query_rows, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, dtype, stream, nullptr);
+}
+
+int pa_prefill_chunk_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* query_start_loc, int32_t total_query_rows,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                         float scale, float k_scale, float v_scale, pa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    const KvScales kv{k_scale, v_scale};
+    return prefill_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, query_start_loc,
+                        total_query_rows, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, scale, dtype, stream, &kv);
 }
 
 }  // extern "C"

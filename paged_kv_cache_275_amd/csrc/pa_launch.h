@@ -86,13 +86,15 @@ struct PrefillArgs {
     int num_q_heads;
     int num_kv_heads;
     int group;          // query heads per kv head
-    float scale_log2;   // scale * log2(e)
+    float scale_log2;   // scale * log2(e) (times k_scale for an fp8 cache)
+    float v_scale;      // fp8 cache: dequantized V = v_scale * stored value (unused otherwise)
 };
 
 // Query heads per prefill column group: a power of two >= group, at most 16.
 constexpr int kPrefillMaxGroup = 16;
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, hipStream_t stream);
+// kv8: the caches hold FP8 E4M3 (k_scale already in scale_log2).
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, bool kv8, hipStream_t stream);
 // Launches the streaming kernel and the split-segment merge.  Non-null events
 // receive the streaming kernel's start and stop times.  kv8: the caches hold
 // FP8 E4M3 (bf16 queries only; 2, 3, 4, 6 or 8 stages).

@@ -34,6 +34,12 @@
 //    the second; V^T is read with the same key order).
 //  * Online softmax per column in the log2 domain; keys past a row's position,
 //    and past the context, are masked (score -inf, V zero).
+//  * FP8 E4M3 caches (KV8): each 8-element chunk is loaded as 8 bytes instead of
+//    16 and converted exactly to bf16 before it is written to LDS, so the tiles
+//    and everything after them are the same; k_scale is folded into the score
+//    scale by the host and v_scale into the final normalisation.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -41,7 +47,7 @@ namespace pa {
 
 constexpr float kSlack = 8.0f;  // log2 units: lazy running max, exp2 <= 256
 
-template <int D, int GP, int NW, int CT>
+template <int D, int GP, int NW, int CT, bool KV8>
 __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs a) {
     constexpr int kCols = NW * 16 * CT;  // (row, head) columns per workgroup
     constexpr int kRT = kCols / GP;      // query rows per workgroup
@@ -94,8 +100,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lg = lane >> 4;    // lane group: k-slots 8*lg .. +8, output rows 4*lg .. +3
     const int lc = lane & 15;    // column within a 16-column tile
-    const uint16_t* kcache = reinterpret_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache);
+    using KVT = typename std::conditional<KV8, uint8_t, uint16_t>::type;  // cache element
+    const KVT* kcache = reinterpret_cast<const KVT*>(a.k_cache);
+    const KVT* vcache = reinterpret_cast<const KVT*>(a.v_cache);
 
     // ---- this lane's columns: query row and head, causal limit, Q^T operands
     int col_row[CT], col_head[CT], col_pos[CT];
@@ -146,7 +153,19 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
     // two tiles in flight
     // native vector registers (a struct copy would be lowered through memory)
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 kreg[2][kKChunks], vreg[2][4];
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    // one 8-element chunk as loaded: 16 bytes of bf16, or 8 bytes of fp8
+    using Chunk = typename std::conditional<KV8, u32x2, u32x4>::type;
+    Chunk kreg[2][kKChunks], vreg[2][4];
+    // a loaded chunk as 8 bf16 (the fp8 conversion is exact)
+    auto widen = [](const Chunk& c) __attribute__((always_inline)) -> u32x4 {
+        if constexpr (KV8) {
+            return u32x4{fp8x2_to_bf16x2<false>(c[0]), fp8x2_to_bf16x2<true>(c[0]), fp8x2_to_bf16x2<false>(c[1]),
+                         fp8x2_to_bf16x2<true>(c[1])};
+        } else {
+            return c;
+        }
+    };
     const int v_kg = tid / (D / 8);   // keys 4*v_kg .. +3 of the tile
     const int v_dc = tid % (D / 8);   // dims 8*v_dc .. +7
     // the four blocks of tile t (the same for the whole workgroup); entries past
@@ -186,28 +205,28 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
         };
 #pragma unroll
         for (int j = 0; j < kKChunks; ++j) {
-            const uint16_t* base = kcache + (size_t)blk(kbi[j]) * blk_stride;
-            kreg[buf][j] = *reinterpret_cast<const u32x4*>(base + koff[j]);
+            const KVT* base = kcache + (size_t)blk(kbi[j]) * blk_stride;
+            kreg[buf][j] = *reinterpret_cast<const Chunk*>(base + koff[j]);
         }
-        const uint16_t* vbase = vcache + (size_t)blk(vbi) * blk_stride;
+        const KVT* vbase = vcache + (size_t)blk(vbi) * blk_stride;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // waves past the V blocks load nothing (uniform per wave: kVBlocks is
             // a multiple of the wave size)
-            if (kVBlocks >= kNT || tid < kVBlocks) vreg[buf][e] = *reinterpret_cast<const u32x4*>(vbase + voff[e]);
+            if (kVBlocks >= kNT || tid < kVBlocks) vreg[buf][e] = *reinterpret_cast<const Chunk*>(vbase + voff[e]);
         }
     };
     auto store_tile = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kKChunks; ++j) {
             const int q = tid + j * kNT;
-            *reinterpret_cast<u32x4*>(&k_lds[(q / (D / 8)) * kKP + (q % (D / 8)) * 8]) = kreg[buf][j];
+            *reinterpret_cast<u32x4*>(&k_lds[(q / (D / 8)) * kKP + (q % (D / 8)) * 8]) = widen(kreg[buf][j]);
         }
         if (tid >= kVBlocks) return;
         // keys past the context: V is zero (the slots may hold anything)
         u32x4 vv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = vreg[buf][e];
+        for (int e = 0; e < 4; ++e) vv[e] = widen(vreg[buf][e]);
         if (t * kKT + kKT > n) {  // uniform: only the tile that reaches past the context
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -372,7 +391,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
         const int i = col_row[ct];
         const int g = col_head[ct];
         if (i0 + i >= c || g >= a.group) continue;
-        const float inv = 1.f / lt;
+        const float inv = (KV8 ? a.v_scale : 1.f) / lt;
         uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
                          ((size_t)(r0 + i0 + i) * a.num_q_heads + hk * a.group + g) * D + 4 * lg;
 #pragma unroll
@@ -385,7 +404,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, int GP>
+template <int D, int GP, bool KV8>
 static hipError_t launch_prefill_g(const PrefillArgs& a, int total_rows, hipStream_t stream) {
     constexpr int kNW = 8, kCT = 2;
     constexpr int kRT = kNW * 16 * kCT / GP;
@@ -394,24 +413,28 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, int total_rows, hipStre
     const long long items = ((long long)total_rows / kRT + a.num_seqs) * a.num_kv_heads;
     const long long grid = (items + 7) / 8 * 8;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<D, GP, kNW, kCT>), dim3((unsigned)grid), dim3(kNW * kWave), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, GP, kNW, kCT, KV8>), dim3((unsigned)grid), dim3(kNW * kWave), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool KV8>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int total_rows, int gp, hipStream_t stream) {
     switch (gp) {
-        case 1: return launch_prefill_g<D, 1>(a, total_rows, stream);
-        case 2: return launch_prefill_g<D, 2>(a, total_rows, stream);
-        case 4: return launch_prefill_g<D, 4>(a, total_rows, stream);
-        case 8: return launch_prefill_g<D, 8>(a, total_rows, stream);
-        default: return launch_prefill_g<D, 16>(a, total_rows, stream);
+        case 1: return launch_prefill_g<D, 1, KV8>(a, total_rows, stream);
+        case 2: return launch_prefill_g<D, 2, KV8>(a, total_rows, stream);
+        case 4: return launch_prefill_g<D, 4, KV8>(a, total_rows, stream);
+        case 8: return launch_prefill_g<D, 8, KV8>(a, total_rows, stream);
+        default: return launch_prefill_g<D, 16, KV8>(a, total_rows, stream);
     }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, hipStream_t stream) {
-    return head_dim == 64 ? launch_prefill_d<64>(a, total_rows, gp, stream)
-                          : launch_prefill_d<128>(a, total_rows, gp, stream);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, int gp, bool kv8, hipStream_t stream) {
+    if (kv8) {
+        return head_dim == 64 ? launch_prefill_d<64, true>(a, total_rows, gp, stream)
+                              : launch_prefill_d<128, true>(a, total_rows, gp, stream);
+    }
+    return head_dim == 64 ? launch_prefill_d<64, false>(a, total_rows, gp, stream)
+                          : launch_prefill_d<128, false>(a, total_rows, gp, stream);
 }
 
 }  // namespace pa

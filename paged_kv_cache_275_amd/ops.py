@@ -78,6 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_prefill_chunk.argtypes = [p, p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32, i64,
                                      f32, ctypes.c_int, p, sz, p]
     lib.pa_prefill_chunk.restype = ctypes.c_int
+    lib.pa_prefill_chunk_fp8.argtypes = [p, p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32, i64,
+                                         f32, f32, f32, ctypes.c_int, p, sz, p]
+    lib.pa_prefill_chunk_fp8.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -407,12 +410,16 @@ def prefill_workspace_size(num_seqs, total_query_rows, num_q_heads, head_dim, ma
 
 
 def _prefill_args(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale, workspace,
-                  stream) -> tuple:
+                  stream, fp8=False) -> tuple:
     import torch
-    _need(q, "q", dim=3)
+    _need(q, "q", torch.bfloat16 if fp8 else None, dim=3)
     _need(out, "out", q.dtype, 3)
-    _need(k_cache, "k_cache", q.dtype, 4)
-    _need(v_cache, "v_cache", q.dtype, 4)
+    if fp8:
+        _need_fp8_cache(k_cache, "k_cache")
+        _need_fp8_cache(v_cache, "v_cache")
+    else:
+        _need(k_cache, "k_cache", q.dtype, 4)
+        _need(v_cache, "v_cache", q.dtype, 4)
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(query_start_loc, "query_start_loc", torch.int32, 1)
     _need(context_lens, "context_lens", torch.int32, 1)
@@ -442,6 +449,17 @@ def prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, conte
     args, _ = _prefill_args(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale,
                             workspace, stream)
     _check(lib, "pa_prefill_chunk", lib.pa_prefill_chunk(*args))
+
+
+def prefill_chunk_fp8(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale: float,
+                      k_scale: float, v_scale: float, workspace=None, stream=None) -> None:
+    """Causal chunked prefill over fp8 caches (pa_prefill_chunk_fp8): q/out bf16
+    [rows, Hq, D], caches uint8 E4M3 bytes with per-tensor scales."""
+    lib = load_library()
+    args, _ = _prefill_args(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale,
+                            workspace, stream, fp8=True)
+    args = args[:16] + (float(k_scale), float(v_scale)) + args[16:]
+    _check(lib, "pa_prefill_chunk_fp8", lib.pa_prefill_chunk_fp8(*args))
 
 
 def bind_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
             "pa_prefill_workspace_size", "pa_status_string", "pa_decode_timed",
             "pa_decode_append", "pa_decode_append_timed", "pa_decode_append_graph", "pa_graph_launch",
             "pa_graph_destroy", "pa_copy_blocks", "pa_bm_create", "pa_bm_append_batch",
-            "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_decode_fp8_timed"} <= set(names)
+            "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_decode_fp8_timed", "pa_prefill_chunk_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"libpa.so does not export {n}"
     out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
@@ -227,3 +227,22 @@ def test_bit_copies_accept_fp8_storage(lib):
     assert lib.pa_reshape_and_cache(None, None, FAKE, FAKE, None, 0, 8, 128, 16, 32, ops.PA_FP8_E4M3, None) == 0
     assert lib.pa_copy_blocks(FAKE, FAKE, None, 0, 8, 64, 16, 32, ops.PA_FP8_E4M3, None) == 0
     assert lib.pa_copy_blocks(FAKE, FAKE, None, 0, 8, 64, 16, 32, 9, None) == ops.PA_EUNSUPPORTED
+
+
+def test_prefill_fp8_rejects(lib):
+    f = lib.pa_prefill_chunk_fp8
+
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=8, qsl=FAKE, rows=64, cl=FAKE,
+                 s=2, hq=32, hkv=8, d=128, bs=16, nb=64, scale=0.1, ks=0.02, vs=0.03, dt=ops.PA_BF16)
+        a.update(kw)
+        return f(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mb"], a["qsl"], a["rows"], a["cl"], a["s"],
+                 a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["ks"], a["vs"], a["dt"], None, 0, None)
+
+    assert call(hq=30) == ops.PA_EINVAL
+    assert call(d=256) == ops.PA_EUNSUPPORTED
+    assert call(dt=ops.PA_F32) == ops.PA_EUNSUPPORTED
+    assert call(rows=0, ks=0.0) == ops.PA_EINVAL           # scale checks before the empty exit
+    assert call(rows=0, vs=float("inf")) == ops.PA_EINVAL
+    assert call(qsl=None) == ops.PA_EINVAL
+    assert call(rows=0, q=None) == ops.PA_OK

@@ -212,3 +212,66 @@ def test_fp8_copy_blocks_bit_exact():
         kc[t] = kc[s]
         vc[t] = vc[s]
     assert to_host(kd).tobytes() == kc.tobytes() and to_host(vd).tobytes() == vc.tobytes()
+
+
+# ---------------------------------------------------------------- chunked prefill
+def test_fp8_prefill_mixed_workload():
+    """The full mixed workload over an fp8 pool: chunk tokens appended with
+    pa_reshape_and_cache_fp8, prefill checked on every row against the oracle."""
+    wl = W.make_workload("mixed_prefill", seed=W.CONFIG_NAMES.index("mixed_prefill"))
+    p = wl.prefill
+    kc = _quantize(wl.k_cache, K_SCALE)
+    vc = _quantize(wl.v_cache, V_SCALE)
+    kc_d, vc_d = to_dev(kc), to_dev(vc)
+    ops.reshape_and_cache_fp8(to_dev(wl.k_new), to_dev(wl.v_new), kc_d, vc_d, to_dev(wl.slot_mapping),
+                              K_SCALE, V_SCALE)
+    out = torch.empty(p.q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.prefill_chunk_fp8(out, to_dev(p.q), kc_d, vc_d, to_dev(p.block_tables), to_dev(p.query_start_loc),
+                          to_dev(p.context_lens), wl.scale, K_SCALE, V_SCALE)
+    torch.cuda.synchronize()
+    F.reshape_and_cache_fp8(_as_f32(wl.k_new), _as_f32(wl.v_new), kc, vc, wl.slot_mapping, K_SCALE, V_SCALE)
+    assert to_host(kc_d).tobytes() == kc.tobytes() and to_host(vc_d).tobytes() == vc.tobytes()
+    print(f"[gpu] fp8 prefill mixed: ctx={p.context_lens.tolist()}", flush=True)
+    ref = F.prefill_fp8(p.q, kc, vc, p.block_tables, p.query_start_loc, p.context_lens, wl.scale, K_SCALE, V_SCALE)
+    mx, rel = assert_attention_close(widen_dev(out), ref, "bf16", "fp8 prefill mixed")
+    print(f"[gpu] fp8 prefill mixed: max-abs {mx:.3e} row-rel {rel:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("hq,hkv,d,chunks,prefixes", [
+    (32, 8, 128, [40, 100], [0, 0]),
+    (32, 8, 128, [33, 7, 65], [300, 17, 64]),
+    (16, 16, 128, [1, 1], [0, 200]),
+    (6, 2, 64, [37, 70], [90, 5]),
+    (32, 2, 64, [20, 9], [3, 1]),
+])
+def test_fp8_prefill_small_full_oracle(hq, hkv, d, chunks, prefixes):
+    """Every row: chunks that are the whole context, ragged chunk lengths, one-row
+    chunks, GQA groups 1, 3, 4 and 16, head_dim 64."""
+    rng = np.random.default_rng(hq * 1000 + d + len(chunks))
+    lens = [c + p for c, p in zip(chunks, prefixes)]
+    q_unused, kc, vc, bt, cl = _random_fp8_case(rng, hq, hkv, d, lens, spare_blocks=6)
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = bf16_bits_from_float(rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32))
+    ks, vs, scale = 1.0 / 256, 1.0 / 300, 0.09
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.prefill_chunk_fp8(out, to_dev(q), to_dev(kc), to_dev(vc), to_dev(bt), to_dev(qsl), to_dev(cl), scale, ks, vs)
+    torch.cuda.synchronize()
+    ref = F.prefill_fp8(q, kc, vc, bt, qsl, cl, scale, ks, vs)
+    assert_attention_close(widen_dev(out), ref, "bf16", f"fp8 prefill chunks={chunks} prefixes={prefixes}")
+
+
+def test_fp8_prefill_one_row_chunks_and_decode_agree_with_oracle():
+    """A one-row chunk is the last row of its sequence and sees the whole context,
+    as a decode query does: both fp8 paths against the same oracle rows."""
+    rng = np.random.default_rng(31)
+    lens = [200, 65]
+    q_dec, kc, vc, bt, cl = _random_fp8_case(rng, 32, 8, 128, lens)
+    qsl = np.array([0, 1, 2], np.int32)
+    ks, vs, scale = 1.0 / 256, 1.0 / 300, 0.09
+    out_p = torch.empty(q_dec.shape, dtype=torch.bfloat16, device="cuda")
+    ops.prefill_chunk_fp8(out_p, to_dev(q_dec), to_dev(kc), to_dev(vc), to_dev(bt), to_dev(qsl), to_dev(cl),
+                          scale, ks, vs)
+    got_d = widen_dev(_decode_fp8_dev(q_dec, kc, vc, bt, cl, scale, ks, vs))
+    ref = F.decode_fp8(q_dec, kc, vc, bt, cl, scale, ks, vs)
+    assert_attention_close(widen_dev(out_p), ref, "bf16", "fp8 prefill one-row chunks")
+    assert_attention_close(got_d, ref, "bf16", "fp8 decode")

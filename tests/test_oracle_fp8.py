@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle.fp8 as F
-from tests._helpers import dense_decode, gather_dense
+from tests._helpers import dense_decode, dense_prefill, gather_dense
 
 torch = pytest.importorskip("torch")
 
@@ -169,3 +169,18 @@ def test_decode_fp8_single_token_is_v_scaled_row():
     got = F.decode_fp8(q, kc, vc, bt, lens, 0.3, 0.5, 0.25)
     row = gather_dense(vc, bt[0], 1)[0]  # [Hkv, D] codes
     assert np.array_equal(got[0], F.E4M3_TABLE[row] * 0.25)
+
+
+def test_prefill_fp8_against_dense_causal_attention():
+    rng = np.random.default_rng(12)
+    ks, vs, scale = 0.004, 0.006, 0.1
+    chunks, prefixes = [5, 19], [0, 30]
+    lens = [c + p for c, p in zip(chunks, prefixes)]
+    q_all, kc, vc, bt, cl = _fp8_case(rng, 8, 2, 64, lens, ks, vs)
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = (rng.standard_normal((int(qsl[-1]), 8, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got = F.prefill_fp8(q, kc, vc, bt, qsl, cl, scale, ks, vs)
+    ref = dense_prefill(q, F.E4M3_TABLE[kc] * ks, F.E4M3_TABLE[vc] * vs, bt, qsl, cl, scale)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    wrong = dense_prefill(q, F.E4M3_TABLE[kc] * vs, F.E4M3_TABLE[vc] * ks, bt, qsl, cl, scale)
+    assert not np.allclose(got, wrong, rtol=1e-3, atol=1e-6)
