@@ -31,17 +31,19 @@
 //    16 bytes), so every fetched line is consumed by a single instruction.
 //  * A ring of STAGES blocks is in flight per wave: the loads of unit x+STAGES
 //    are issued as soon as unit x has been consumed (unconditionally, so that
-//    the hardware load counter only has to drain to the stage being consumed).  Block ids (and the valid
-//    token count of each block) are staged per wave in LDS up front, so no load
-//    waits on a block-table read.  Each block's query rows are loaded with its
-//    K/V (bf16 path): hardware load counters drain in issue order, so a query
-//    load issued outside the ring would force the whole ring to land at every
-//    switch of segment.
-//  * Scores: v_dot2_f32_bf16 partial dot products, summed over the 8 lanes of
-//    a token group by three DPP adds.  Online softmax in the log2 domain with a
-//    wave-uniform running max per head that is only raised when a block holds
-//    a score more than kRescaleSlack above it (ballot -> uniform branch): the
-//    same softmax, with rare accumulator rescales and exp2 <= 2^kRescaleSlack.
+//    the hardware load counter only has to drain to the stage being
+//    consumed).  Block ids (and the valid token count of each block) are
+//    staged per wave in LDS up front, so no load waits on a block-table read.
+//    Each block's query rows are loaded with its K/V (bf16 path): hardware
+//    load counters drain in issue order, so a query load issued outside the
+//    ring would force the whole ring to land at every switch of segment.
+//  * Scores: bf16 on the matrix cores (Q, GP heads padded to 16 rows, times
+//    K^T of the block's 16 tokens); fp32 by FMA dot products summed over the 8
+//    lanes of a token group by three DPP adds.  Online softmax in the log2
+//    domain with a wave-uniform running max per head that is only raised when
+//    a block holds a score more than kRescaleSlack above it (ballot -> uniform
+//    branch): the same softmax, with rare accumulator rescales and
+//    exp2 <= 2^kRescaleSlack.
 //  * P*V: probabilities packed to bf16 pairs (token tg, token tg+8); V
 //    re-paired by v_perm so one v_dot2 adds both tokens.  The normaliser is
 //    summed from the same rounded probabilities.
@@ -53,9 +55,17 @@
 //    kernel costs a launch; merging in place would need an agent-scope
 //    release/acquire pair per split segment, which on this chip writes back
 //    and invalidates a whole L2 and measured far slower.
+//  * Finished segments wait in LDS and are written after the wave's last load:
+//    a store in mid-stream would hold up the completion count of the loads
+//    issued after it.
 //  * Tokens >= n in a sequence's last block are masked (score -inf, V zeroed),
 //    so stale slots -- even NaN -- never reach the result.  Sequences with no
 //    tokens get zero rows.
+//  * Fused append (pa_decode_append): the unit holding a sequence's new token
+//    reads that token's K/V rows from the inputs; the merge kernel copies them
+//    into the cache afterwards.
+//  * FP8 E4M3 caches (KV8 instances): the same kernel on byte caches, the bytes
+//    converted exactly to bf16 operands; see decode_stream_kernel.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
