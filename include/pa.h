@@ -73,7 +73,8 @@ typedef enum {
     PA_EUNSUPPORTED = -2, /* valid, but a shape or dtype this build does not handle */
     PA_EWORKSPACE = -3,   /* workspace pointer NULL or smaller than required */
     PA_ELAUNCH = -4,      /* the HIP runtime refused a launch */
-    PA_ENOMEM = -5        /* block manager: not enough free blocks (nothing changed) */
+    PA_ENOMEM = -5        /* block manager: not enough free blocks, or no host memory
+                             left (nothing changed) */
 } pa_status;
 
 /*

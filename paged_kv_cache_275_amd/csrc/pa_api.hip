@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "pa.h"
 #include "pa_launch.h"
@@ -87,15 +88,17 @@ int env_int(const char* name, int fallback, int lo = 1) {
 // the current device.  PA_DECODE_WAVES overrides the count (launch-shape
 // sweeps and tests); it is read on every call.
 int decode_waves(int per_cu) {
-    static int cached_cus[64] = {0};
+    // compute units per device, looked up once (any thread may fill a slot;
+    // all write the same value)
+    static std::atomic<int> cached_cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     const int slot = dev < 64 ? dev : 63;
-    int cus = cached_cus[slot];
+    int cus = cached_cus[slot].load(std::memory_order_relaxed);
     if (cus <= 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        cached_cus[slot] = cus;
+        cached_cus[slot].store(cus, std::memory_order_relaxed);
     }
     long long w = (long long)cus * per_cu;
     if (const char* env = getenv("PA_DECODE_WAVES")) {

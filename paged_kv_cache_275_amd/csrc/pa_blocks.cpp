@@ -16,7 +16,9 @@
 //    allocation pops, release pushes (most recently freed block reused first);
 //  * a sequence's blocks are released from its last block to its first;
 //  * an operation that cannot get all the blocks it needs fails with
-//    PA_ENOMEM and changes nothing.
+//    PA_ENOMEM and changes nothing.  So does one that runs out of host memory:
+//    every allocation is made before the first change, and no C++ exception
+//    crosses the C ABI.
 #include <stdint.h>
 
 #include <new>
@@ -59,10 +61,15 @@ pa_block_manager* pa_bm_create(int64_t num_blocks, int32_t block_size) {
     if (num_blocks <= 0 || num_blocks > INT32_MAX / kBlockTokens || block_size != kBlockTokens) return nullptr;
     pa_block_manager* m = new (std::nothrow) pa_block_manager;
     if (!m) return nullptr;
-    m->num_blocks = num_blocks;
-    m->refcount.assign((size_t)num_blocks, 0);
-    m->free_stack.reserve((size_t)num_blocks);
-    for (int64_t b = num_blocks - 1; b >= 0; --b) m->free_stack.push_back((int32_t)b);
+    try {
+        m->num_blocks = num_blocks;
+        m->refcount.assign((size_t)num_blocks, 0);
+        m->free_stack.reserve((size_t)num_blocks);  // release never reallocates
+        for (int64_t b = num_blocks - 1; b >= 0; --b) m->free_stack.push_back((int32_t)b);
+    } catch (...) {
+        delete m;
+        return nullptr;
+    }
     return m;
 }
 
@@ -75,11 +82,15 @@ int pa_bm_add_sequence(pa_block_manager* m, int64_t seq_id, int64_t num_tokens) 
     if (m->seqs.count(seq_id)) return PA_EINVAL;
     const int64_t need = (num_tokens + kBlockTokens - 1) / kBlockTokens;
     if (need > (int64_t)m->free_stack.size()) return PA_ENOMEM;
-    Seq s;
-    s.tokens = num_tokens;
-    s.blocks.reserve((size_t)need);
-    for (int64_t i = 0; i < need; ++i) s.blocks.push_back(m->pop());
-    m->seqs.emplace(seq_id, std::move(s));
+    try {
+        Seq s;
+        s.tokens = num_tokens;
+        s.blocks.reserve((size_t)need);
+        Seq& dst = m->seqs.emplace(seq_id, std::move(s)).first->second;  // allocations done
+        for (int64_t i = 0; i < need; ++i) dst.blocks.push_back(m->pop());
+    } catch (...) {
+        return PA_ENOMEM;
+    }
     return PA_OK;
 }
 
@@ -87,9 +98,13 @@ int pa_bm_fork(pa_block_manager* m, int64_t parent_id, int64_t child_id) {
     if (!m || parent_id == child_id) return PA_EINVAL;
     auto it = m->seqs.find(parent_id);
     if (it == m->seqs.end() || m->seqs.count(child_id)) return PA_EINVAL;
-    Seq child = it->second;  // same blocks, same tokens
-    for (int32_t b : child.blocks) ++m->refcount[b];
-    m->seqs.emplace(child_id, std::move(child));
+    try {
+        Seq child = it->second;  // same blocks, same tokens
+        const Seq& c = m->seqs.emplace(child_id, std::move(child)).first->second;  // allocations done
+        for (int32_t b : c.blocks) ++m->refcount[b];
+    } catch (...) {
+        return PA_ENOMEM;
+    }
     return PA_OK;
 }
 
@@ -109,10 +124,10 @@ int64_t pa_bm_num_tokens(const pa_block_manager* m, int64_t seq_id) {
     return it == m->seqs.end() ? -1 : it->second.tokens;
 }
 
-int pa_bm_append_batch(pa_block_manager* m, const int64_t* seq_ids, int32_t n, int32_t* slot_mapping,
-                       int32_t* copies, int32_t max_copies, int32_t* num_copies) {
-    if (!m || n < 0 || (n > 0 && (!seq_ids || !slot_mapping)) || max_copies < 0 || !num_copies) return PA_EINVAL;
-    if (max_copies > 0 && !copies) return PA_EINVAL;
+namespace {
+
+int append_batch(pa_block_manager* m, const int64_t* seq_ids, int32_t n, int32_t* slot_mapping, int32_t* copies,
+                 int32_t max_copies, int32_t* num_copies) {
     // Check first, replaying the batch on the reference counts alone: every id
     // known and distinct, enough free blocks and copy room.  (A shared block
     // copied away by one sequence may be left to a single owner, who then
@@ -140,9 +155,14 @@ int pa_bm_append_batch(pa_block_manager* m, const int64_t* seq_ids, int32_t n, i
     }
     if (need_blocks > (int64_t)m->free_stack.size()) return PA_ENOMEM;
     if (need_copies > max_copies) return PA_EINVAL;
+    // room for the new last blocks, so that nothing below allocates
+    for (int32_t i = 0; i < n; ++i) {
+        Seq& s = m->seqs.find(seq_ids[i])->second;
+        if (s.tokens % kBlockTokens == 0) s.blocks.reserve(s.blocks.size() + 1);
+    }
     int32_t nc = 0;
     for (int32_t i = 0; i < n; ++i) {
-        Seq& s = m->seqs[seq_ids[i]];
+        Seq& s = m->seqs.find(seq_ids[i])->second;
         if (s.tokens % kBlockTokens == 0) {
             s.blocks.push_back(m->pop());
         } else if (m->refcount[s.blocks.back()] > 1) {
@@ -159,6 +179,19 @@ int pa_bm_append_batch(pa_block_manager* m, const int64_t* seq_ids, int32_t n, i
     }
     *num_copies = nc;
     return PA_OK;
+}
+
+}  // namespace
+
+int pa_bm_append_batch(pa_block_manager* m, const int64_t* seq_ids, int32_t n, int32_t* slot_mapping,
+                       int32_t* copies, int32_t max_copies, int32_t* num_copies) {
+    if (!m || n < 0 || (n > 0 && (!seq_ids || !slot_mapping)) || max_copies < 0 || !num_copies) return PA_EINVAL;
+    if (max_copies > 0 && !copies) return PA_EINVAL;
+    try {
+        return append_batch(m, seq_ids, n, slot_mapping, copies, max_copies, num_copies);
+    } catch (...) {  // only the checks allocate (their maps): nothing has changed
+        return PA_ENOMEM;
+    }
 }
 
 int pa_bm_batch_tables(const pa_block_manager* m, const int64_t* seq_ids, int32_t n, int32_t* block_tables,
