@@ -1045,9 +1045,9 @@ static hipError_t launch_decode_g(const DecodeArgs& a, int stages, bool kv8, hip
         }
     } else {
         switch (stages) {
-            case 2: e = launch_stream<T, D, GP, 2, false>(a, stream, ev_start, ev_stop); break;
             case 3: e = launch_stream<T, D, GP, 3, false>(a, stream, ev_start, ev_stop); break;
-            default: e = launch_stream<T, D, GP, 4, false>(a, stream, ev_start, ev_stop); break;
+            case 4: e = launch_stream<T, D, GP, 4, false>(a, stream, ev_start, ev_stop); break;
+            default: e = launch_stream<T, D, GP, 2, false>(a, stream, ev_start, ev_stop); break;
         }
     }
     if (e != hipSuccess) return e;

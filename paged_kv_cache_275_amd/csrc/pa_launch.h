@@ -11,7 +11,10 @@ namespace pa {
 // block) units with kDecodeStages blocks in flight; block ids are staged in
 // LDS kDecodeWindow units at a time.
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeStages = 4;      // default; 2 and 3 are also built (fp8 caches: 2, 3, 6, 8)
+// Default ring depth: 2 blocks per wave measured best (llama3_8b 91.8 vs
+// 92.7 us at 4, qwen3_0p6b 33.5 vs 34.6 us); 3 and 4 are also built (fp8
+// caches: 2, 3, 4, 6, 8).
+constexpr int kDecodeStages = 2;
 constexpr int kDecodeWindow = 256;
 constexpr int kDecodeWavesPerCU = 4;
 // An fp8 cache halves the bytes per unit but not the instructions: with two

@@ -194,6 +194,16 @@ def test_invalid_arguments_raise():
     assert e.value.status == ops.PA_EINVAL
 
 
+@pytest.mark.parametrize("stages", ["2", "3", "4"])
+def test_decode_ring_depths(stages, monkeypatch):
+    """Every built ring depth (PA_DECODE_STAGES) gives a correct result, fused
+    and unfused, also for a context of many windows."""
+    monkeypatch.setenv("PA_DECODE_STAGES", stages)
+    wl = W.make_workload("llama3_8b", seed=51, num_seqs=10)
+    _check_workload(wl, f"stages={stages}")
+    _check_fused(W.make_workload("long_skewed", seed=52, num_seqs=2), f"stages={stages}/long")
+
+
 @pytest.mark.parametrize("waves", ["4", "8", "60", "4096"])
 def test_decode_launch_shapes(waves, monkeypatch):
     """The result must not depend on how the units are split over waves: one

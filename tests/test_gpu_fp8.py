@@ -275,3 +275,12 @@ def test_fp8_prefill_one_row_chunks_and_decode_agree_with_oracle():
     ref = F.decode_fp8(q_dec, kc, vc, bt, cl, scale, ks, vs)
     assert_attention_close(widen_dev(out_p), ref, "bf16", "fp8 prefill one-row chunks")
     assert_attention_close(got_d, ref, "bf16", "fp8 decode")
+
+
+@pytest.mark.parametrize("stages,waves", [("2", "1024"), ("3", "2048"), ("4", "2048"), ("6", "1024"), ("8", "1024")])
+def test_fp8_ring_depths_and_launch_shapes(stages, waves, monkeypatch):
+    """Every ring depth built for fp8 caches, with one and two waves per SIMD."""
+    monkeypatch.setenv("PA_DECODE_STAGES", stages)
+    monkeypatch.setenv("PA_DECODE_WAVES", waves)
+    wl = W.make_workload("llama3_8b", seed=61, num_seqs=10)
+    _check_fp8(wl, f"stages={stages}/waves={waves}")
