@@ -746,6 +746,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                 if (ux >= wn) break;
                 const int ug = wb0 + ux;
                 const bool seg_end = (cblk == cnb - 1) || (ug == u_end - 1);
+                // the table entry of the unit this stage is refilled with, read
+                // now so that its LDS latency hides behind this unit's work
+                const uint4 e_refill = tab[min(ux + STAGES, wn - 1)];
                 const bool has_next = seg_end && (ug + 1 < u_end);
                 int ns = cs;
                 if (has_next) {
@@ -872,7 +875,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 
                 // ---- refill this stage (unconditionally, see above)
                 __builtin_amdgcn_sched_barrier(0);
-                issue(st, tab[min(ux + STAGES, wn - 1)]);
+                issue(st, e_refill);
                 __builtin_amdgcn_sched_barrier(0);
 
                 if (!seg_end) {
