@@ -330,3 +330,76 @@ def test_decode_append_max_sequences(hq, hkv, d):
     assert np.all(got[lens == 0] == 0.0)
     ref = oracle.decode(q, okc, ovc, bt, lens, scale)
     assert_attention_close(got, ref, "bf16", f"fused S=8192 hq{hq}/hkv{hkv}/d{d}")
+
+
+# ---------------------------------------------------------------- large pools and groups
+def _scatter_to_big_pool(kc_small, vc_small, bt_small, nb_big, rng):
+    """Place the blocks of a compact pool at chosen ids of a pool of nb_big
+    blocks (allocated on the GPU, never read elsewhere).  Returns the device
+    caches and the remapped block table; the oracle keeps the compact pool
+    (its result does not depend on block ids)."""
+    nb_small = kc_small.shape[0]
+    # half the blocks beyond 4 GiB of byte offset, half near the start
+    hi = rng.choice(np.arange(nb_big - 4096, nb_big), size=nb_small - nb_small // 2, replace=False)
+    lo = rng.choice(np.arange(0, 4096), size=nb_small // 2, replace=False)
+    new_id = np.concatenate([lo, hi]).astype(np.int64)
+    rng.shuffle(new_id)
+    bt_big = np.where(bt_small >= 0, new_id[np.maximum(bt_small, 0)], -1).astype(np.int32)
+    from tests._gpu import to_dev
+    shape = (nb_big,) + kc_small.shape[1:]
+    dt = torch.bfloat16 if kc_small.dtype == np.uint16 else torch.uint8
+    kbig = torch.empty(shape, dtype=dt, device="cuda")
+    vbig = torch.empty(shape, dtype=dt, device="cuda")
+    idx = torch.from_numpy(new_id).cuda()
+    kbig[idx] = to_dev(kc_small)
+    vbig[idx] = to_dev(vc_small)
+    return kbig, vbig, bt_big
+
+
+def test_decode_and_prefill_in_a_pool_beyond_4gib():
+    """Blocks whose byte offsets exceed 2^32 (a 6 GiB pool per cache): every
+    address computation must be 64-bit.  Unfused and fused decode, and prefill."""
+    from tests._gpu import to_dev
+    rng = np.random.default_rng(4242)
+    hq, hkv, d = 32, 8, 128
+    lens = [300, 1, 17, 1000]
+    q, kc, vc, bt, cl = _random_bf16_case(rng, hq, hkv, d, lens, spare_blocks=2)
+    nb_big = 196608                                   # 32 KiB blocks: 6 GiB per cache
+    assert (nb_big - 4096) * 16 * hkv * d * 2 > 2 ** 32
+    kbig, vbig, bt_big = _scatter_to_big_pool(kc, vc, bt, nb_big, rng)
+    print(f"[gpu] pool beyond 4 GiB: {kbig.numel() * 2 / 2**30:.1f} GiB per cache", flush=True)
+    ref = oracle.decode(q, kc, vc, bt, cl, 0.09)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.decode(out, to_dev(q), kbig, vbig, to_dev(bt_big), to_dev(cl), 0.09)
+    torch.cuda.synchronize()
+    assert_attention_close(widen_dev(out), ref, "bf16", "decode, pool > 4 GiB")
+    # fused: the new token of each sequence goes to a slot beyond 4 GiB or near 0
+    key = _bf16_bits(rng, (len(lens), hkv, d))
+    value = _bf16_bits(rng, (len(lens), hkv, d))
+    okc, ovc = kc.copy(), vc.copy()
+    slots = np.array([int(bt[i, (n - 1) // 16]) * 16 + (n - 1) % 16 for i, n in enumerate(lens)], np.int32)
+    oracle.reshape_and_cache(key, value, okc, ovc, slots)
+    ops.decode_append(out, to_dev(q), to_dev(key), to_dev(value), kbig, vbig, to_dev(bt_big), to_dev(cl), 0.09)
+    torch.cuda.synchronize()
+    assert_attention_close(widen_dev(out), oracle.decode(q, okc, ovc, bt, cl, 0.09), "bf16", "fused, pool > 4 GiB")
+    big_slots = [int(bt_big[i, (n - 1) // 16]) * 16 + (n - 1) % 16 for i, n in enumerate(lens)]
+    for i, sl in enumerate(big_slots):
+        got = kbig.view(-1, hkv, d)[sl].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, key[i]), f"appended K row {i} (slot {sl})"
+    # prefill: the last 40 tokens of sequence 3 as a chunk over the same pool
+    qsl = np.array([0, 40], np.int32)
+    pq = _bf16_bits(rng, (40, hq, d))
+    pout = torch.empty((40, hq, d), dtype=torch.bfloat16, device="cuda")
+    ops.prefill_chunk(pout, to_dev(pq), kbig, vbig, to_dev(bt_big[3:4]), to_dev(qsl), to_dev(cl[3:4]), 0.09)
+    torch.cuda.synchronize()
+    pref = oracle.prefill(pq, okc, ovc, bt[3:4], qsl, cl[3:4], 0.09)
+    assert_attention_close(widen_dev(pout), pref, "bf16", "prefill, pool > 4 GiB")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(64, 1, 128), (128, 2, 64)])
+def test_decode_largest_group(hq, hkv, d):
+    """64 query heads per kv head, the most a call takes (8 head groups of 8)."""
+    rng = np.random.default_rng(hq + d)
+    q, kc, vc, bt, lens = _random_bf16_case(rng, hq, hkv, d, [1, 50, 700], spare_blocks=5)
+    got = _decode_bf16(q, kc, vc, bt, lens, 0.07)
+    assert_attention_close(got, oracle.decode(q, kc, vc, bt, lens, 0.07), "bf16", f"group {hq // hkv}")

@@ -284,3 +284,28 @@ def test_fp8_ring_depths_and_launch_shapes(stages, waves, monkeypatch):
     monkeypatch.setenv("PA_DECODE_WAVES", waves)
     wl = W.make_workload("llama3_8b", seed=61, num_seqs=10)
     _check_fp8(wl, f"stages={stages}/waves={waves}")
+
+
+def test_fp8_decode_in_a_pool_beyond_4gib_and_largest_group():
+    """fp8 blocks (16 KiB at this shape) placed beyond 2^32 bytes of a 5 GiB pool
+    per cache, and a group of 64 query heads per kv head."""
+    rng = np.random.default_rng(777)
+    hq, hkv, d = 64, 8, 128
+    lens = [33, 400, 1]
+    q, kc, vc, bt, cl = _random_fp8_case(rng, hq, hkv, d, lens, spare_blocks=2)
+    nb_big = 327680
+    assert (nb_big - 4096) * 16 * hkv * d > 2 ** 32
+    nb_small = kc.shape[0]
+    hi = rng.choice(np.arange(nb_big - 4096, nb_big), size=nb_small, replace=False)
+    bt_big = np.where(bt >= 0, hi[np.maximum(bt, 0)], -1).astype(np.int32)
+    kbig = torch.empty((nb_big, 16, hkv, d), dtype=torch.uint8, device="cuda")
+    vbig = torch.empty_like(kbig)
+    idx = torch.from_numpy(hi.astype(np.int64)).cuda()
+    kbig[idx] = to_dev(kc)
+    vbig[idx] = to_dev(vc)
+    ks, vs, scale = 1.0 / 256, 1.0 / 300, 0.09
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.decode_fp8(out, to_dev(q), kbig, vbig, to_dev(bt_big), to_dev(cl), scale, ks, vs)
+    torch.cuda.synchronize()
+    ref = F.decode_fp8(q, kc, vc, bt, cl, scale, ks, vs)
+    assert_attention_close(widen_dev(out), ref, "bf16", "fp8, pool > 4 GiB, group 64")
