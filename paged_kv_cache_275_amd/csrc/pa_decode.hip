@@ -908,98 +908,111 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 // Merge the partial records of the split segment noted by wave w (if any):
 //   M = max_v m_v,  L = sum_v l_v 2^(m_v - M),  out = sum_v acc_v 2^(m_v - M) / L
 // over the waves v = w, w + n_kvg, ..., last_wave (the waves of the segment's
-// head group in consecutive wave groups) that hold its units.  One workgroup per
-// noting wave, one wave per head; every record load is independent of the
-// others, so a merge costs two dependent memory round trips (the note, then
-// the records).
+// head group in consecutive wave groups) that hold its units, folded in record
+// order with a running maximum.  One workgroup per noting wave, one wave per
+// head.  The note is one memory round trip; the (max, sum) pairs and sums of up
+// to kBatch records are then loaded together, so a merge of up to kBatch parts
+// costs two dependent round trips.  In the fused call the workgroup first
+// copies new K/V rows into the cache (see below).  Records of zero weight (m = -inf: waves
+// whose range was empty) are skipped without touching their sums.
 template <typename T, int D, int GP>
 __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) {
-    if (a.new_k != nullptr) {
-        // Fused KV append: the new token's K/V rows of some sequences go to
-        // their cache slots (position N-1).  The streaming kernel took those
-        // rows from the inputs, so the copies only have to be done by the end
-        // of the call; here they cost the streaming waves nothing.
-        constexpr int kRowVecsPerHead = D * (int)sizeof(T) / 16;
-        const int row_vecs = a.num_kv_heads * kRowVecsPerHead;
-        for (int sq = blockIdx.x; sq < a.num_seqs; sq += gridDim.x) {
-            const int nq = a.context_lens[sq];
-            if (nq <= 0) continue;
-            const int bq = a.block_tables[(size_t)sq * a.max_blocks_per_seq + (nq - 1) / kBlockTokens];
-            const size_t slot = (size_t)bq * kBlockTokens + (nq - 1) % kBlockTokens;
-            const uint4* ksrc = reinterpret_cast<const uint4*>(a.new_k) + (size_t)sq * row_vecs;
-            const uint4* vsrc = reinterpret_cast<const uint4*>(a.new_v) + (size_t)sq * row_vecs;
-            uint4* kdst = reinterpret_cast<uint4*>(a.k_cache_w) + slot * row_vecs;
-            uint4* vdst = reinterpret_cast<uint4*>(a.v_cache_w) + slot * row_vecs;
-            for (int i = threadIdx.x; i < row_vecs; i += blockDim.x) {
-                kdst[i] = ksrc[i];
-                vdst[i] = vsrc[i];
-            }
-        }
-    }
+    constexpr int kPerLane = D / kWave;  // 1 or 2
+    constexpr int kBatch = 8;
     const int w = blockIdx.x;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
     const SplitNote sn = a.ws_split[w];
-    if (sn.seq < 0) return;
-    const int nrec = (sn.last_wave - w) / a.n_kvg + 1;  // waves w, w + n_kvg, ..., last_wave
-    const int gi0 = (sn.kvg % a.groups_per_kv) * GP;
-    const int hk = sn.kvg / a.groups_per_kv;
-    constexpr int kPerLane = D / kWave;  // 1 or 2
-    constexpr int kBatch = 8;
-    auto rec_of = [&](int j, int g) -> size_t {  // record of wave w + j * n_kvg, head g
+    const int gi0 = sn.seq >= 0 ? (sn.kvg % a.groups_per_kv) * GP : 0;
+    const bool merging = sn.seq >= 0 && gi0 + g < a.group;
+    const int nrec = merging ? (sn.last_wave - w) / a.n_kvg + 1 : 1;  // waves w, w + n_kvg, ..., last_wave
+    auto rec_of = [&](int j) __attribute__((always_inline)) -> size_t {  // record of wave w + j * n_kvg, head g
         return ((size_t)(w + j * a.n_kvg) * 2 + (j == 0 ? sn.first_slot : 0)) * GP + g;
     };
-    {
-        if (gi0 + g >= a.group) return;
-        // lane j: (max, sum) of record j (chunks of 64 records)
-        float M = -INFINITY;
-        for (int j = lane; j < nrec; j += kWave) M = fmaxf(M, a.ws_ml[rec_of(j, g) * 2]);
+    // lane b loads the (max, sum) of record j0 + b (one vector load for the
+    // batch), every lane its kPerLane sums of each record; records past nrec
+    // repeat the last one and get zero weight, so every load is used and all
+    // are issued before the first wait
+    float2 mlv;
+    float x[kBatch][kPerLane];
+    auto load_batch = [&](int j0) __attribute__((always_inline)) {
+        mlv = *reinterpret_cast<const float2*>(a.ws_ml + rec_of(min(j0 + (lane & (kBatch - 1)), nrec - 1)) * 2);
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        float L = 0.f;
-        float o[kPerLane];
+        for (int b = 0; b < kBatch; ++b) {
+            const size_t r = rec_of(min(j0 + b, nrec - 1));
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) o[i] = 0.f;
-        for (int j0 = 0; j0 < nrec; j0 += kWave) {
-            float swj = 0.f, lj = 0.f;
-            if (j0 + lane < nrec) {
-                const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + rec_of(j0 + lane, g) * 2);
-                swj = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
-                lj = ml.y;
-            }
-            L += lj * swj;
-            const int cnt = min(kWave, nrec - j0);
-            for (int b0 = 0; b0 < cnt; b0 += kBatch) {
-                float x[kBatch][kPerLane];
-#pragma unroll
-                for (int b = 0; b < kBatch; ++b) {
-                    const bool ok = b0 + b < cnt;
-                    const size_t r = rec_of(ok ? j0 + b0 + b : 0, g);
-#pragma unroll
-                    for (int i = 0; i < kPerLane; ++i) x[b][i] = a.ws_acc[r * D + lane * kPerLane + i];
-                }
-#pragma unroll
-                for (int b = 0; b < kBatch; ++b) {
-                    const float sw = __shfl(swj, (b0 + b) & (kWave - 1));
-                    if (b0 + b < cnt && sw != 0.f) {
-#pragma unroll
-                        for (int i = 0; i < kPerLane; ++i) o[i] += x[b][i] * sw;
-                    }
-                }
+            for (int i = 0; i < kPerLane; ++i) x[b][i] = a.ws_acc[r * D + lane * kPerLane + i];
+        }
+    };
+    if (merging) load_batch(0);  // in flight while the copy below resolves its slot
+
+    if (a.new_k != nullptr) {
+        // Fused KV append: the new token's K/V rows of sequence w (and w +
+        // gridDim.x, ...) go to their cache slots (position N-1).  The streaming
+        // kernel took those rows from the inputs, so the copies only have to be
+        // done by the end of the call.  The rows and the context length load
+        // together with the records above; the copy adds the block-table read.
+        constexpr int kRowVecsPerHead = D * (int)sizeof(T) / 16;
+        // four vectors per thread and chunk, in named registers (an array
+        // here would be placed in memory before the loops are unrolled)
+        const int row_vecs = a.num_kv_heads * kRowVecsPerHead;
+        const int bd = (int)blockDim.x;
+        const int chunk = 4 * bd;  // one chunk at the configurations' shapes
+        for (int sq = w; sq < a.num_seqs; sq += gridDim.x) {
+            const uint4* ksrc = reinterpret_cast<const uint4*>(a.new_k) + (size_t)sq * row_vecs;
+            const uint4* vsrc = reinterpret_cast<const uint4*>(a.new_v) + (size_t)sq * row_vecs;
+            for (int c0 = 0; c0 < row_vecs; c0 += chunk) {
+                const int i0 = c0 + (int)threadIdx.x, i1 = i0 + bd, i2 = i1 + bd, i3 = i2 + bd;
+                const int last = row_vecs - 1;
+                const uint4 k0 = ksrc[min(i0, last)], k1 = ksrc[min(i1, last)];
+                const uint4 k2 = ksrc[min(i2, last)], k3 = ksrc[min(i3, last)];
+                const uint4 v0 = vsrc[min(i0, last)], v1 = vsrc[min(i1, last)];
+                const uint4 v2 = vsrc[min(i2, last)], v3 = vsrc[min(i3, last)];
+                const int nq = a.context_lens[sq];
+                if (nq <= 0) break;
+                const int bq = a.block_tables[(size_t)sq * a.max_blocks_per_seq + (nq - 1) / kBlockTokens];
+                const size_t slot = (size_t)bq * kBlockTokens + (nq - 1) % kBlockTokens;
+                uint4* kdst = reinterpret_cast<uint4*>(a.k_cache_w) + slot * row_vecs;
+                uint4* vdst = reinterpret_cast<uint4*>(a.v_cache_w) + slot * row_vecs;
+                if (i0 < row_vecs) { kdst[i0] = k0; vdst[i0] = v0; }
+                if (i1 < row_vecs) { kdst[i1] = k1; vdst[i1] = v1; }
+                if (i2 < row_vecs) { kdst[i2] = k2; vdst[i2] = v2; }
+                if (i3 < row_vecs) { kdst[i3] = k3; vdst[i3] = v3; }
             }
         }
+    }
+    if (!merging) return;
+
+    const int hk = sn.kvg / a.groups_per_kv;
+    float M = -INFINITY, L = 0.f, o[kPerLane];
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-        const float inv = 1.f / L;
-        T* orow = reinterpret_cast<T*>(a.out) + ((size_t)sn.seq * a.num_q_heads + hk * a.group + gi0 + g) * D +
-                  lane * kPerLane;
+    for (int i = 0; i < kPerLane; ++i) o[i] = 0.f;
+    for (int j0 = 0; j0 < nrec; j0 += kBatch) {
+        if (j0 > 0) load_batch(j0);
+        float2 ml[kBatch];
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            if constexpr (sizeof(T) == 2) {
-                reinterpret_cast<uint16_t*>(orow)[i] = f32_to_bf16_bits(o[i] * inv);
-            } else {
-                reinterpret_cast<float*>(orow)[i] = o[i] * inv;
-            }
+        for (int b = 0; b < kBatch; ++b) ml[b] = make_float2(readlane_f32(mlv.x, b), readlane_f32(mlv.y, b));
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const bool live = j0 + b < nrec && ml[b].x != -INFINITY;
+            const float mn = live ? fmaxf(M, ml[b].x) : M;
+            const float ca = live ? fast_exp2(M - mn) : 1.f;  // 0 while M is -inf
+            const float cb = live ? fast_exp2(ml[b].x - mn) : 0.f;
+            L = L * ca + (live ? ml[b].y * cb : 0.f);
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) o[i] = o[i] * ca + (live ? x[b][i] * cb : 0.f);
+            M = mn;
+        }
+    }
+    const float inv = 1.f / L;
+    T* orow = reinterpret_cast<T*>(a.out) + ((size_t)sn.seq * a.num_q_heads + hk * a.group + gi0 + g) * D +
+              lane * kPerLane;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        if constexpr (sizeof(T) == 2) {
+            reinterpret_cast<uint16_t*>(orow)[i] = f32_to_bf16_bits(o[i] * inv);
+        } else {
+            reinterpret_cast<float*>(orow)[i] = o[i] * inv;
         }
     }
 }

@@ -403,3 +403,42 @@ def test_decode_largest_group(hq, hkv, d):
     q, kc, vc, bt, lens = _random_bf16_case(rng, hq, hkv, d, [1, 50, 700], spare_blocks=5)
     got = _decode_bf16(q, kc, vc, bt, lens, 0.07)
     assert_attention_close(got, oracle.decode(q, kc, vc, bt, lens, 0.07), "bf16", f"group {hq // hkv}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_workspace_reused(fused):
+    """One workspace across calls of different shapes, largest first: each call
+    matches the oracle, whatever earlier calls left in the workspace.  The
+    shapes split contexts over a handful of waves, over every wave of the grid
+    (65536 tokens), and over waves whose share is smaller than one block."""
+    from tests._gpu import to_dev
+    rng = np.random.default_rng(8080 + fused)
+    hq, hkv, d = 32, 8, 128
+    ws = torch.zeros(ops.decode_workspace_size(64, hq, hkv, d, 4096), dtype=torch.uint8, device="cuda")
+    cases = [[65536, 3000, 17, 1, 64],
+             rng.integers(1, 3000, 48).tolist(),
+             [40, 1, 300, 5],
+             [1, 1, 2]]
+    for i, lens in enumerate(cases):
+        print(f"[gpu] workspace reuse fused={fused} case={i} lens={lens[:6]}", flush=True)
+        q, kc, vc, bt, lens_a = _random_bf16_case(rng, hq, hkv, d, lens)
+        scale = 1.0 / np.sqrt(d)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        dkc, dvc = to_dev(kc), to_dev(vc)
+        if fused:
+            s = len(lens_a)
+            key = _bf16_bits(rng, (s, hkv, d))
+            value = _bf16_bits(rng, (s, hkv, d))
+            slots = np.array([int(bt[j, (n - 1) // 16]) * 16 + (n - 1) % 16 for j, n in enumerate(lens_a)],
+                             np.int32)
+            ops.decode_append(out, to_dev(q), to_dev(key), to_dev(value), dkc, dvc, to_dev(bt), to_dev(lens_a),
+                              scale, workspace=ws)
+            oracle.reshape_and_cache(key, value, kc, vc, slots)
+        else:
+            ops.decode(out, to_dev(q), dkc, dvc, to_dev(bt), to_dev(lens_a), scale, workspace=ws)
+        torch.cuda.synchronize()
+        if fused:
+            assert to_host(dkc).tobytes() == kc.tobytes()
+            assert to_host(dvc).tobytes() == vc.tobytes()
+        ref = oracle.decode(q, kc, vc, bt, lens_a, scale)
+        assert_attention_close(widen_dev(out), ref, "bf16", f"workspace reuse case {i}")
