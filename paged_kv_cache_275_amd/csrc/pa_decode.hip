@@ -29,6 +29,7 @@
 //    group read one contiguous 128-byte line of the token's row (16 bytes per
 //    lane); chunk c of lane dl holds dims c*8*E + dl*E .. +E (E = elements per
 //    16 bytes), so every fetched line is consumed by a single instruction.
+//  * K/V are loaded with the non-temporal hint (read once, never reused).
 //  * A ring of STAGES blocks is in flight per wave: the loads of unit x+STAGES
 //    are issued as soon as unit x has been consumed (unconditionally, so that
 //    the hardware load counter only has to drain to the stage being
@@ -622,10 +623,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                 kb = reinterpret_cast<const KVT*>(a.new_k) + (size_t)nrow * D + 8 * mrow;
             if constexpr (KV8) {
 #pragma unroll
-                for (int p = 0; p < kMf / 2; ++p) kb4[st][p] = *reinterpret_cast<const uint4*>(kb + 64 * p);
+                for (int p = 0; p < kMf / 2; ++p) kb4[st][p] = ldg_nt(kb + 64 * p);
             } else {
 #pragma unroll
-                for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = *reinterpret_cast<const uint4*>(kb + 32 * mm);
+                for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = ldg_nt(kb + 32 * mm);
             }
             // the unit's query rows travel with its K/V: no load outside the ring
             // ever has to be waited for (loads complete in issue order)
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
                 for (int c = 0; c < kVecs; ++c)
-                    kr[st][t][c] = *reinterpret_cast<const uint4*>((t == 0 ? kt0 : kt1) + c * 8 * kE);
+                    kr[st][t][c] = ldg_nt((t == 0 ? kt0 : kt1) + c * 8 * kE);
             }
         }
 #pragma unroll
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             } else {
 #pragma unroll
                 for (int c = 0; c < kVecs; ++c)
-                    vr[st][t][c] = *reinterpret_cast<const uint4*>((t == 0 ? vb0 : vb1) + c * 8 * kE);
+                    vr[st][t][c] = ldg_nt((t == 0 ? vb0 : vb1) + c * 8 * kE);
             }
         }
     };

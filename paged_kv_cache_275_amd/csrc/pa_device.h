@@ -108,6 +108,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load with the non-temporal hint (global_load ... nt): for data read
+// exactly once, such as the KV stream of decode.  Measured on llama3_8b decode:
+// about 2 us of 93 faster than plain loads.
+__device__ __forceinline__ uint4 ldg_nt(const void* p) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---- FP8 E4M3 (OCP "E4M3FN": bias 7, largest finite 448, no infinities).
 // gfx950's conversions use this format and round to nearest even; a value
 // beyond +-448 would become NaN, so quantization clamps first.
