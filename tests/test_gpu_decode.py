@@ -442,3 +442,36 @@ def test_decode_workspace_reused(fused):
             assert to_host(dvc).tobytes() == vc.tobytes()
         ref = oracle.decode(q, kc, vc, bt, lens_a, scale)
         assert_attention_close(widen_dev(out), ref, "bf16", f"workspace reuse case {i}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("f32", 16, 16), ("bf16", 32, 32)])
+def test_decode_append_many_kv_heads(dtype, hq, hkv):
+    """Fused append with one query head per kv head and many kv heads: a new
+    token's K row (Hkv * D * e bytes, 512 vectors of 16 bytes here) is wider
+    than one pass of the merge workgroup's copy (4 vectors for each of its 64
+    threads), so the copy into the cache takes several chunks."""
+    from tests._gpu import to_dev
+    rng = np.random.default_rng(515 + hq)
+    d = 128
+    lens = [1, 17, 40, 200, 33]
+    print(f"[gpu] fused many kv heads dtype={dtype} hq={hq} hkv={hkv}", flush=True)
+    q, kc, vc, bt, lens_a = _random_bf16_case(rng, hq, hkv, d, lens)
+    s = len(lens_a)
+    key = _bf16_bits(rng, (s, hkv, d))
+    value = _bf16_bits(rng, (s, hkv, d))
+    if dtype == "f32":  # the same values, exactly, as fp32 (NaN poison stays NaN)
+        def f32(x):
+            return (x.astype(np.uint32) << 16).view(np.float32)
+        q, kc, vc, key, value = f32(q), f32(kc), f32(vc), f32(key), f32(value)
+    slots = np.array([int(bt[j, (n - 1) // 16]) * 16 + (n - 1) % 16 for j, n in enumerate(lens_a)], np.int32)
+    dkc, dvc = to_dev(kc), to_dev(vc)
+    dq = to_dev(q)
+    out = torch.empty_like(dq)
+    scale = 1.0 / np.sqrt(d)
+    ops.decode_append(out, dq, to_dev(key), to_dev(value), dkc, dvc, to_dev(bt), to_dev(lens_a), scale)
+    torch.cuda.synchronize()
+    oracle.reshape_and_cache(key, value, kc, vc, slots)
+    assert to_host(dkc).tobytes() == kc.tobytes()
+    assert to_host(dvc).tobytes() == vc.tobytes()
+    ref = oracle.decode(q, kc, vc, bt, lens_a, scale)
+    assert_attention_close(widen_dev(out), ref, dtype, f"fused many kv heads {dtype}")
