@@ -53,9 +53,10 @@
 //    in the workspace (slot 0: the wave's first segment, slot 1: its last) and
 //    the wave holding its first unit notes it; decode_fixup_kernel then merges
 //    the records of each noted segment (log-sum-exp).  Merging in a second
-//    kernel costs a launch; merging in place would need an agent-scope
-//    release/acquire pair per split segment, which on this chip writes back
-//    and invalidates a whole L2 and measured far slower.
+//    kernel costs a launch.  Merging in place (coherent record stores and an
+//    arrival counter per segment, the last wave to arrive merging) measured
+//    slower: a segment's first part is the last thing its wave streams, so
+//    nearly every wave would end with the merge's dependent memory round trips.
 //  * Finished segments wait in LDS and are written after the wave's last load:
 //    a store in mid-stream would hold up the completion count of the loads
 //    issued after it.
