@@ -312,6 +312,39 @@ def prefill_flops(wl) -> int:
     return 4 * wl.head_dim * wl.num_q_heads * pairs
 
 
+def stream_reference(stream, nbytes=4 << 30, reps=10):
+    """Reference streaming rates measured on the same GPU in the same run, over
+    nbytes (16 times the MALL; long enough that the kernel's start and end
+    cost little), outside the timed region:
+    a plain read (pa_stream_read_probe: every 16-byte vector loaded once, as
+    the decode kernel loads K and V, without the gather) and a device-to-device
+    copy (read + write bytes).  Returns (read GB/s, copy GB/s)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_275_amd import ops
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    xor_out = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+    read_us = timed(lambda: ops.stream_read_probe(src, xor_out, stream))
+    copy_us = timed(lambda: dst.copy_(src))
+    del src, dst
+    return nbytes / (read_us * 1e-6) / 1e9, 2 * nbytes / (copy_us * 1e-6) / 1e9
+
+
 def copy_calibration():
     """A plain device-to-device copy of CALIB_BYTES, three times, for counter scaling."""
     import torch
@@ -583,6 +616,16 @@ def main():
         pf = prefill_flops(wl)
         res["timing_us"]["prefill_tflops"] = round(pf / (float(prefill_us.mean()) * 1e-6) / 1e12, 2)
     res["extras"] = extras(wl, pools[0][0], pools[0][1], stream)
+    read_gbs, copy_gbs = stream_reference(stream)
+    res["extras"]["stream_read_gbs"] = round(read_gbs, 1)
+    res["extras"]["stream_copy_gbs"] = round(copy_gbs, 1)
+    res["extras"]["dominant_kernel_frac_of_stream_read"] = (
+        round(res["roofline"]["achieved"] / read_gbs, 4) if res["roofline"]["unit"] == "GB/s" else None)
+    res["extras"]["stream_reference_note"] = ("plain streaming over 4 GiB on the same GPU in the same run, median of "
+                                              "10: pa_stream_read_probe (read bytes; the same 16-byte non-temporal "
+                                              "loads as the decode kernel, without the gather) and a torch "
+                                              "device-to-device copy (read + write bytes), for context beside the "
+                                              "8 TB/s peak")
     if not args.unfused:
         res["extras"].update(graph_step(wl, pools, pre, out, q, k_new[t_new - s_dec:], v_new[t_new - s_dec:], bt, cl,
                                         ws, stream))

@@ -313,6 +313,18 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t n
                    int64_t num_blocks, pa_dtype dtype, void *stream);
 
 /*
+ * Streaming-read reference for benchmarks (not part of attention): reads every
+ * byte of src once, 16 bytes per load with the non-temporal hint as the decode
+ * kernel loads K and V, and XORs every 32-bit word of it into *xor_out (device
+ * memory, which the caller sets before the call; zero gives the XOR of src).
+ * The bytes read divided by the kernel's time is the plain read rate the gather
+ * of the decode kernel is compared with.  bytes must be a multiple of 16 and src
+ * 16-byte aligned (PA_EINVAL otherwise); bytes == 0 is a no-op.  Asynchronous on
+ * stream; allocates nothing.
+ */
+int pa_stream_read_probe(const void *src, size_t bytes, uint32_t *xor_out, void *stream);
+
+/*
  * Host block manager (CPU only, no device memory): hands out the pool's block
  * ids to sequences and builds the block tables, context lengths and slot
  * mappings the kernels above take.  A sequence gets a new block only when its

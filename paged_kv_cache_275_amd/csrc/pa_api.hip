@@ -184,6 +184,13 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
+int pa_stream_read_probe(const void* src, size_t bytes, uint32_t* xor_out, void* stream) {
+    if (bytes == 0) return PA_OK;
+    if (!src || !xor_out || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0) return PA_EINVAL;
+    hipError_t e = pa::launch_stream_read_probe(src, bytes, xor_out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size) {
     (void)max_blocks_per_seq;

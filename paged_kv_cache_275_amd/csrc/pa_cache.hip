@@ -140,3 +140,45 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
 }
 
 }  // namespace pa
+
+namespace pa {
+
+// One streaming read of a buffer, the reference read rate of the benchmark:
+// every 16-byte vector is loaded once with the non-temporal hint (as the
+// decode stream loads K and V), eight in flight per thread, and every 32-bit
+// word is folded by XOR into *xor_out.  The fold keeps the loads and gives a
+// result a test can check exactly.
+__global__ __launch_bounds__(256) void stream_read_probe_kernel(const uint4* __restrict__ src, long long n_vec,
+                                                                uint32_t* __restrict__ xor_out) {
+    constexpr int kU = 8;
+    uint32_t acc = 0;
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (kU - 1) * stride < n_vec; i += kU * stride) {
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = ldg_nt(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n_vec; i += stride) {
+        const uint4 v = ldg_nt(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off);
+    if ((threadIdx.x & (kWave - 1)) == 0 && acc != 0) atomicXor(xor_out, acc);
+}
+
+hipError_t launch_stream_read_probe(const void* src, size_t bytes, uint32_t* xor_out, hipStream_t stream) {
+    const long long n_vec = (long long)(bytes / 16);
+    long long blocks = (n_vec + 255) / 256;
+    // 16 workgroups of 4 waves per compute unit: 6.45 TB/s over 4 GiB, against
+    // 6.27 with 8 and 5.74 with 4 (plain loads instead of non-temporal: 5.64)
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(stream_read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint4*>(src), n_vec, xor_out);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -112,6 +112,7 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
                                         const int32_t* slot_mapping, int num_tokens, int row_elems, bool src_bf16,
                                         float k_inv, float v_inv, hipStream_t stream);
+hipError_t launch_stream_read_probe(const void* src, size_t bytes, uint32_t* xor_out, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs, int block_bytes,
                               hipStream_t stream);
 

@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_prefill_chunk_fp8.argtypes = [p, p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32, i64,
                                          f32, f32, f32, ctypes.c_int, p, sz, p]
     lib.pa_prefill_chunk_fp8.restype = ctypes.c_int
+    lib.pa_stream_read_probe.argtypes = [p, sz, p, p]
+    lib.pa_stream_read_probe.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -474,3 +476,16 @@ def bind_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, 
     def call(_keep=ws):
         _check(lib, "pa_prefill_chunk", fn(*args))
     return call
+
+
+def stream_read_probe(src, xor_out, stream=None) -> None:
+    """pa_stream_read_probe: one streaming read of the contiguous device tensor
+    src (a multiple of 16 bytes), XOR-folding its 32-bit words into xor_out (a
+    one-element int32 device tensor the caller sets; zero gives the XOR of src)."""
+    import torch
+    if not src.is_contiguous() or xor_out.dtype != torch.int32 or xor_out.numel() < 1:
+        raise ValueError("src must be contiguous and xor_out a one-element int32 tensor")
+    lib = load_library()
+    _check(lib, "pa_stream_read_probe",
+           lib.pa_stream_read_probe(src.data_ptr(), src.numel() * src.element_size(), xor_out.data_ptr(),
+                                    _stream_handle(src, stream)))

@@ -246,3 +246,13 @@ def test_prefill_fp8_rejects(lib):
     assert call(rows=0, vs=float("inf")) == ops.PA_EINVAL
     assert call(qsl=None) == ops.PA_EINVAL
     assert call(rows=0, q=None) == ops.PA_OK
+
+
+def test_stream_read_probe_argument_checks(lib):
+    """Rejected on the host before any HIP call: null pointers, a size that is
+    not a multiple of 16, a misaligned source; zero bytes is a no-op."""
+    assert lib.pa_stream_read_probe(None, 64, FAKE, None) == ops.PA_EINVAL
+    assert lib.pa_stream_read_probe(FAKE, 64, None, None) == ops.PA_EINVAL
+    assert lib.pa_stream_read_probe(FAKE, 24, FAKE, None) == ops.PA_EINVAL
+    assert lib.pa_stream_read_probe(ctypes.c_void_p(0x1008), 64, FAKE, None) == ops.PA_EINVAL
+    assert lib.pa_stream_read_probe(None, 0, None, None) == ops.PA_OK
