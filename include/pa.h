@@ -229,6 +229,20 @@ int pa_decode_append_timed(void *out, const void *q, const void *key, const void
                            void *kernel_start, void *kernel_stop);
 
 /*
+ * Launch shape of every later pa_decode* call in this process (all threads):
+ * waves of the persistent streaming grid (0 = 4 per compute unit, 8 for an fp8
+ * cache when two workgroups fit a compute unit; at most 4096, rounded down to a
+ * multiple of 4), blocks in flight per wave (0 = the default 2; else 2, 3 or 4,
+ * and for fp8 caches also 6 or 8) and the extra work-split cost of closing a
+ * sequence in units of a quarter block (-1 = the default 4; else 0..64).  The
+ * results of decode do not depend on these choices; they move only the split
+ * points and the pipeline depth.  For tests and launch-shape sweeps; calls
+ * already enqueued are unaffected.  PA_EINVAL for values out of range (nothing
+ * changes then).
+ */
+int pa_decode_set_launch(int32_t waves, int32_t stages, int32_t switch_ticks);
+
+/*
  * The decode step as a HIP graph, for callers that repeat it on fixed buffers
  * (the CUDA-graph-style launch the pages list among an engine's speed-ups:
  * page "vllm-v0 版本介绍", section 为什么需要推理框架？, item 3).

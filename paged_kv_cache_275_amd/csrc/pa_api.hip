@@ -76,17 +76,14 @@ DecodeWsLayout decode_ws_layout(int gp, int32_t head_dim) {
     return L;
 }
 
-// Integer from the environment if set and >= lo, else fallback.
-int env_int(const char* name, int fallback, int lo = 1) {
-    const char* v = getenv(name);
-    if (!v) return fallback;
-    const int x = atoi(v);
-    return x >= lo ? x : fallback;
-}
+// Launch-shape overrides set by pa_decode_set_launch (0: the built-in
+// default).  Process-wide; read with relaxed loads on every decode call.
+std::atomic<int> g_override_waves{0};
+std::atomic<int> g_override_stages{0};
+std::atomic<int> g_override_switch_ticks{-1};
 
-// Waves of the persistent decode grid: per_cu per compute unit of
-// the current device.  PA_DECODE_WAVES overrides the count (launch-shape
-// sweeps and tests); it is read on every call.
+// Waves of the persistent decode grid: per_cu per compute unit of the
+// current device, unless pa_decode_set_launch chose a count.
 int decode_waves(int per_cu) {
     // compute units per device, looked up once (any thread may fill a slot;
     // all write the same value)
@@ -101,10 +98,8 @@ int decode_waves(int per_cu) {
         cached_cus[slot].store(cus, std::memory_order_relaxed);
     }
     long long w = (long long)cus * per_cu;
-    if (const char* env = getenv("PA_DECODE_WAVES")) {
-        const long long e = atoll(env);
-        if (e > 0) w = e;
-    }
+    const int ov = g_override_waves.load(std::memory_order_relaxed);
+    if (ov > 0) w = ov;
     if (w > pa::kDecodeMaxWaves) w = pa::kDecodeMaxWaves;
     w = (w / pa::kDecodeWaves) * pa::kDecodeWaves;
     if (w < pa::kDecodeWaves) w = pa::kDecodeWaves;
@@ -114,6 +109,16 @@ int decode_waves(int per_cu) {
 }  // namespace
 
 extern "C" {
+
+int pa_decode_set_launch(int32_t waves, int32_t stages, int32_t switch_ticks) {
+    if (waves < 0 || waves > pa::kDecodeMaxWaves) return PA_EINVAL;
+    if (stages != 0 && stages != 2 && stages != 3 && stages != 4 && stages != 6 && stages != 8) return PA_EINVAL;
+    if (switch_ticks < -1 || switch_ticks > 64) return PA_EINVAL;
+    g_override_waves.store(waves, std::memory_order_relaxed);
+    g_override_stages.store(stages, std::memory_order_relaxed);
+    g_override_switch_ticks.store(switch_ticks, std::memory_order_relaxed);
+    return PA_OK;
+}
 
 const char* pa_status_string(int status) {
     switch (status) {
@@ -270,15 +275,15 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.wave_groups = std::max(1, std::min(decode_waves(per_cu), pa::kDecodeMaxWaves) / a.n_kvg);
     if ((long long)a.wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
     a.waves = a.wave_groups * a.n_kvg;
-    // PA_DECODE_SWITCH_TICKS (0..64) overrides the segment cost, for sweeps
     a.unit_ticks = pa::kDecodeUnitTicks;
-    a.switch_ticks = std::min(64, env_int("PA_DECODE_SWITCH_TICKS", pa::kDecodeSwitchTicks, 0));
+    const int ov_ticks = g_override_switch_ticks.load(std::memory_order_relaxed);
+    a.switch_ticks = ov_ticks >= 0 ? ov_ticks : pa::kDecodeSwitchTicks;
     a.scale_log2 = (kv8 ? scale * kv8->k : scale) * 1.4426950408889634f;
     a.v_scale = kv8 ? kv8->v : 1.0f;
-    // PA_DECODE_STAGES (2, 3 or 4; fp8 caches also 6 or 8) selects the
-    // pipeline depth, for sweeps
-    const int stages = env_int("PA_DECODE_STAGES", per_cu == pa::kDecodeWavesPerCUFp8 ? pa::kDecodeStagesFp8Pair
-                                                                                        : pa::kDecodeStages);
+    const int ov_stages = g_override_stages.load(std::memory_order_relaxed);
+    const int stages = ov_stages > 0 ? ov_stages
+                                     : (per_cu == pa::kDecodeWavesPerCUFp8 ? pa::kDecodeStagesFp8Pair
+                                                                           : pa::kDecodeStages);
     hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, kv8 != nullptr,
                                      static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(kernel_start), static_cast<hipEvent_t>(kernel_stop));

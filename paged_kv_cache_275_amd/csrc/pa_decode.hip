@@ -71,6 +71,7 @@
 #include <hip/hip_ext.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -78,6 +79,17 @@
 namespace pa {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: lazy max, exp2 <= 256
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order, each with a
+// compile-time index (an unrolled loop whatever the body's size).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Finished segments are staged in LDS and written out once the wave's loads are
 // done (see the kernel).  A slot holds one segment: a header of 4 words, two
@@ -229,6 +241,21 @@ __device__ __forceinline__ void pv_block(float (&acc)[GP][KDPL], float (&l)[GP],
                 }
             }
         }
+    }
+}
+
+// Pins values in VGPRs at this point in program order: whatever computes them
+// must run before it.  Placed after the P*V products of a ring stage, ahead of
+// that stage's refill: without it the compiler sinks the products below the
+// refill, the refilled V registers then need copies at the loop back edge, and
+// each copy waits for its load -- which drains the whole ring once per unit.
+template <int GP, int KDPL>
+__device__ __forceinline__ void keep_in_regs(float (&acc)[GP][KDPL], float (&l)[GP]) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        asm volatile("" : "+v"(l[g]));
+#pragma unroll
+        for (int d = 0; d < KDPL; ++d) asm volatile("" : "+v"(acc[g][d]));
     }
 }
 
@@ -570,6 +597,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // every counter to zero: the stores above are a variable number, and
+        // without a known count after them the compiler's waits for the ring
+        // stages would turn conservative everywhere after this point
+        __builtin_amdgcn_s_waitcnt(0);
     };
 
     uint32_t qb[GP][kQb], qnb[GP][kQb];
@@ -736,16 +767,12 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         // each stage's loads together and in ring order.  The number of loads in
         // flight is then the same on all paths, and the compiler's wait counts
         // only wait for the stage being consumed, not for the whole ring.
-#pragma unroll
-        for (int st = 0; st < STAGES; ++st) {
-            issue(st, tab[min(st, wn - 1)]);
+        static_for<STAGES>([&](auto st) {
+            issue(st, tab[min((int)st, wn - 1)]);
             __builtin_amdgcn_sched_barrier(0);
-        }
-        for (int x = 0; x < wn; x += STAGES) {
-#pragma unroll
-            for (int st = 0; st < STAGES; ++st) {
-                const int ux = x + st;
-                if (ux >= wn) break;
+        });
+        // One unit: consume ring stage st (window unit ux), then refill it.
+        auto unit_step = [&](const int st, const int ux) __attribute__((always_inline)) {
                 const int ug = wb0 + ux;
                 const bool seg_end = (cblk == cnb - 1) || (ug == u_end - 1);
                 // the table entry of the unit this stage is refilled with, read
@@ -875,14 +902,16 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                     pv_block<T, GP, kDpl, kVecs>(acc, l, p, vr[st]);
                 }
 
-                // ---- refill this stage (unconditionally, see above)
+                // ---- refill this stage (unconditionally, see above), once its
+                // registers are no longer read
+                keep_in_regs<GP, kDpl>(acc, l);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(st, e_refill);
                 __builtin_amdgcn_sched_barrier(0);
 
                 if (!seg_end) {
                     ++cblk;
-                    continue;
+                    return;
                 }
                 finish_segment();
                 if (has_next) {
@@ -900,8 +929,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                         }
                     }
                 }
-            }
+        };
+        // Whole rounds of the ring, with no exit inside a round: on every path
+        // through the loop the stages are consumed and refilled in ring order,
+        // so the compiler's load-counter waits at a stage only cover that
+        // stage's loads.  (A conditional exit between stages gives the wait
+        // placement paths on which a later stage's loads look the most recent,
+        // and it then waits for the whole ring before every unit.)
+        int x = 0;
+        for (; x + STAGES <= wn; x += STAGES) {
+            static_for<STAGES>([&](auto st) { unit_step(st, x + st); });
         }
+        // the last wn % STAGES units of the window
+        static_for<STAGES - 1>([&](auto st) {
+            if (x + st < wn) unit_step(st, x + st);
+        });
     }
     flush();
     if (lane == 0) a.ws_split[wv] = note;

@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_prefill_chunk_fp8.restype = ctypes.c_int
     lib.pa_stream_read_probe.argtypes = [p, sz, p, p]
     lib.pa_stream_read_probe.restype = ctypes.c_int
+    lib.pa_decode_set_launch.argtypes = [i32, i32, i32]
+    lib.pa_decode_set_launch.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -210,12 +212,20 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blo
                                                        head_dim, max_blocks_per_seq, block_size))
 
 
-def decode_workspace(q, k_cache, block_tables):
-    """Allocate a workspace (torch, uint8) big enough for decode() with these shapes."""
+def decode_workspace(q, k_cache, block_tables, stream=None):
+    """Allocate a workspace (torch, uint8) big enough for decode() with these shapes.
+
+    With a stream other than the current one, the allocation is marked as in
+    use by that stream (record_stream): the caching allocator then keeps the
+    memory until the work enqueued there has finished, even when the caller
+    drops the tensor right after enqueueing."""
     import torch
     n = decode_workspace_size(q.shape[0], q.shape[1], k_cache.shape[2], q.shape[2],
                               block_tables.shape[1], k_cache.shape[1])
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace, stream) -> tuple:
@@ -233,7 +243,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, wo
     if block_tables.shape[0] != s or context_lens.shape[0] != s:
         raise ValueError("block_tables and context_lens need one row per sequence")
     if workspace is None:
-        workspace = decode_workspace(q, k_cache, block_tables)
+        workspace = decode_workspace(q, k_cache, block_tables, stream)
     args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), s,
             hq, hkv, d, bs, nb, float(scale), _dtype_code(q), workspace.data_ptr(),
@@ -296,7 +306,7 @@ def _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     if block_tables.shape[0] != s or context_lens.shape[0] != s:
         raise ValueError("block_tables and context_lens need one row per sequence")
     if workspace is None:
-        workspace = decode_workspace(q, k_cache, block_tables)
+        workspace = decode_workspace(q, k_cache, block_tables, stream)
     args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), s,
             hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale), PA_BF16, workspace.data_ptr(),
@@ -435,6 +445,8 @@ def _prefill_args(out, q, k_cache, v_cache, block_tables, query_start_loc, conte
     need = prefill_workspace_size(sp, rows, hq, d, block_tables.shape[1], bs)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if stream is not None:
+            workspace.record_stream(stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -476,6 +488,29 @@ def bind_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, 
     def call(_keep=ws):
         _check(lib, "pa_prefill_chunk", fn(*args))
     return call
+
+
+def set_decode_launch(waves: int = 0, stages: int = 0, switch_ticks: int = -1) -> None:
+    """pa_decode_set_launch: launch shape of later decode calls in this process
+    (0 / 0 / -1 restore the defaults)."""
+    lib = load_library()
+    _check(lib, "pa_decode_set_launch", lib.pa_decode_set_launch(int(waves), int(stages), int(switch_ticks)))
+
+
+class decode_launch:
+    """Context manager: decode calls inside use this launch shape; the defaults
+    are restored on exit."""
+
+    def __init__(self, waves: int = 0, stages: int = 0, switch_ticks: int = -1):
+        self.shape = (waves, stages, switch_ticks)
+
+    def __enter__(self):
+        set_decode_launch(*self.shape)
+        return self
+
+    def __exit__(self, *exc):
+        set_decode_launch()
+        return False
 
 
 def stream_read_probe(src, xor_out, stream=None) -> None:

@@ -13,6 +13,7 @@ import pytest
 import oracle
 from paged_kv_cache_275_amd import ops
 from paged_kv_cache_275_amd import workloads as W
+from tests import _oracle_threads as oracle_threads
 from tests._gpu import DevWorkload, to_host, widen_dev
 from tests._helpers import assert_attention_close, widen
 
@@ -37,14 +38,17 @@ def _run_append_and_decode(wl):
     return dw
 
 
-def _check_workload(wl, label):
+def _check_workload(wl, label, threaded=False):
     print(f"[gpu] {label}: S={wl.num_seqs} sumN={int(wl.context_lens.sum())} "
           f"NB={wl.num_blocks} dtype={wl.dtype}", flush=True)
     dw = _run_append_and_decode(wl)
     kc, vc = _oracle_pool_after_append(wl)
     assert to_host(dw.k_cache).tobytes() == kc.tobytes(), f"{label}: K cache differs"
     assert to_host(dw.v_cache).tobytes() == vc.tobytes(), f"{label}: V cache differs"
-    ref = oracle.decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale)
+    if threaded:
+        ref = oracle_threads.decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale)
+    else:
+        ref = oracle.decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale)
     got = widen_dev(dw.out)
     mx, rel = assert_attention_close(got, ref, wl.dtype, label)
     print(f"[gpu] {label}: max-abs {mx:.3e} row-rel {rel:.3e}", flush=True)
@@ -62,11 +66,13 @@ def test_decode_small(name, num_seqs, seed):
     _check_workload(wl, f"{name}/s{seed}/n{num_seqs}")
 
 
-# Full-size workloads, exactly as the bench builds them (seed = config index).
+# Full-size workloads, exactly as the bench builds them (seed = config index),
+# and the same shapes at seeds + 100 and + 200.
 @pytest.mark.parametrize("name", list(W.CONFIG_NAMES))
-def test_decode_full_size(name):
-    wl = W.make_workload(name, seed=W.CONFIG_NAMES.index(name))
-    _check_workload(wl, f"{name}/full")
+@pytest.mark.parametrize("seed_offset", [0, 100, 200])
+def test_decode_full_size(name, seed_offset):
+    wl = W.make_workload(name, seed=W.CONFIG_NAMES.index(name) + seed_offset)
+    _check_workload(wl, f"{name}/full/+{seed_offset}", threaded=True)
 
 
 def test_decode_deterministic_and_block_permutation_invariant():
@@ -177,11 +183,11 @@ def test_decode_max_sequences(hq, hkv, d):
 
 
 @pytest.mark.parametrize("ticks", ["0", "1", "64"])
-def test_decode_switch_cost_does_not_change_results(ticks, monkeypatch):
+def test_decode_switch_cost_does_not_change_results(ticks):
     """The segment cost only moves the split points between wave groups."""
-    monkeypatch.setenv("PA_DECODE_SWITCH_TICKS", ticks)
     wl = W.make_workload("llama3_8b", seed=31, num_seqs=40)
-    _check_workload(wl, f"switch_ticks={ticks}")
+    with ops.decode_launch(switch_ticks=int(ticks)):
+        _check_workload(wl, f"switch_ticks={ticks}")
 
 
 def test_invalid_arguments_raise():
@@ -195,25 +201,25 @@ def test_invalid_arguments_raise():
 
 
 @pytest.mark.parametrize("stages", ["2", "3", "4"])
-def test_decode_ring_depths(stages, monkeypatch):
-    """Every built ring depth (PA_DECODE_STAGES) gives a correct result, fused
-    and unfused, also for a context of many windows."""
-    monkeypatch.setenv("PA_DECODE_STAGES", stages)
+def test_decode_ring_depths(stages):
+    """Every built ring depth (pa_decode_set_launch) gives a correct result,
+    fused and unfused, also for a context of many windows."""
     wl = W.make_workload("llama3_8b", seed=51, num_seqs=10)
-    _check_workload(wl, f"stages={stages}")
-    _check_fused(W.make_workload("long_skewed", seed=52, num_seqs=2), f"stages={stages}/long")
+    with ops.decode_launch(stages=int(stages)):
+        _check_workload(wl, f"stages={stages}")
+        _check_fused(W.make_workload("long_skewed", seed=52, num_seqs=2), f"stages={stages}/long")
 
 
 @pytest.mark.parametrize("waves", ["4", "8", "60", "4096"])
-def test_decode_launch_shapes(waves, monkeypatch):
+def test_decode_launch_shapes(waves):
     """The result must not depend on how the units are split over waves: one
     workgroup (several LDS windows per wave), few waves, an odd count and the
     largest grid (mostly empty ranges)."""
-    monkeypatch.setenv("PA_DECODE_WAVES", waves)
-    wl = W.make_workload("llama3_8b", seed=21, num_seqs=12)
-    _check_workload(wl, f"waves={waves}")
-    wl = W.make_workload("long_skewed", seed=22, num_seqs=2)
-    _check_workload(wl, f"waves={waves}/long")
+    with ops.decode_launch(waves=int(waves)):
+        wl = W.make_workload("llama3_8b", seed=21, num_seqs=12)
+        _check_workload(wl, f"waves={waves}")
+        wl = W.make_workload("long_skewed", seed=22, num_seqs=2)
+        _check_workload(wl, f"waves={waves}/long")
 
 
 # ---------------------------------------------------------------- fused append

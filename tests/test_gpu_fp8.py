@@ -165,21 +165,21 @@ def test_fp8_single_token_returns_scaled_v_exactly(d):
         assert np.array_equal(got[s], np.repeat(v, 4, axis=0)), f"sequence {s}"
 
 
-def test_fp8_unit_scales_match_bf16_decode(monkeypatch):
+def test_fp8_unit_scales_match_bf16_decode():
     """With k_scale = v_scale = 1 the fp8 path and the bf16 path see the same
     numbers (every E4M3 value is a bf16).  On the same split of the work over
     waves (the fp8 path otherwise runs twice as many) they differ only in the
     order of fp32 sums, so the outputs agree to 2 bf16 units in the last place."""
-    monkeypatch.setenv("PA_DECODE_WAVES", "1024")
     rng = np.random.default_rng(77)
     q, kc, vc, bt, lens = _random_fp8_case(rng, 32, 8, 128, [1, 16, 17, 200, 1000, 2500])
     scale = 1.0 / 2048
-    got8 = widen_dev(_decode_fp8_dev(q, kc, vc, bt, lens, scale, 1.0, 1.0))
     kb = bf16_bits_from_float(np.nan_to_num(F.E4M3_TABLE[kc], nan=0.0).astype(np.float32))
     vb = bf16_bits_from_float(np.nan_to_num(F.E4M3_TABLE[vc], nan=0.0).astype(np.float32))
     out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
-    ops.decode(out, to_dev(q), to_dev(kb), to_dev(vb), to_dev(bt), to_dev(lens), scale)
-    torch.cuda.synchronize()
+    with ops.decode_launch(waves=1024):
+        got8 = widen_dev(_decode_fp8_dev(q, kc, vc, bt, lens, scale, 1.0, 1.0))
+        ops.decode(out, to_dev(q), to_dev(kb), to_dev(vb), to_dev(bt), to_dev(lens), scale)
+        torch.cuda.synchronize()
     got16 = widen_dev(out)
     tol = 2.0 ** -6 * np.maximum(np.abs(got8), np.abs(got16)) + 1e-6
     assert np.all(np.abs(got8 - got16) <= tol), float(np.max(np.abs(got8 - got16) - tol))
@@ -278,12 +278,11 @@ def test_fp8_prefill_one_row_chunks_and_decode_agree_with_oracle():
 
 
 @pytest.mark.parametrize("stages,waves", [("2", "1024"), ("3", "2048"), ("4", "2048"), ("6", "1024"), ("8", "1024")])
-def test_fp8_ring_depths_and_launch_shapes(stages, waves, monkeypatch):
+def test_fp8_ring_depths_and_launch_shapes(stages, waves):
     """Every ring depth built for fp8 caches, with one and two waves per SIMD."""
-    monkeypatch.setenv("PA_DECODE_STAGES", stages)
-    monkeypatch.setenv("PA_DECODE_WAVES", waves)
     wl = W.make_workload("llama3_8b", seed=61, num_seqs=10)
-    _check_fp8(wl, f"stages={stages}/waves={waves}")
+    with ops.decode_launch(waves=int(waves), stages=int(stages)):
+        _check_fp8(wl, f"stages={stages}/waves={waves}")
 
 
 def test_fp8_decode_in_a_pool_beyond_4gib_and_largest_group():
