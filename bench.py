@@ -435,6 +435,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama3_8b")
     ap.add_argument("--rotate", type=int, default=4, help="independent KV pool copies")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="bracket the dominant kernel with timing events on every N-th timed step")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
@@ -561,12 +563,19 @@ def main():
         kernels["prefill_kernel"] = float(prefill_us.mean())
     dom = max(kernels, key=kernels.get)
 
-    # timed region: exactly K steps; only the dominant kernel is bracketed
-    tev = [new_events(2) for _ in range(args.steps)]
+    # timed region: exactly K steps.  The dominant kernel is bracketed by
+    # events on every event_every-th step only: timing events cost the GPU a
+    # few microseconds per bracketed launch (measured 3-4 us per decode call),
+    # which would otherwise be counted in every step.
+    every = max(1, args.event_every)
+    tev = [new_events(2) for _ in range((args.steps + every - 1) // every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i, e in enumerate(tev):
-        if dom == "decode_stream_kernel":
+    for i in range(args.steps):
+        e = tev[i // every] if i % every == 0 else None
+        if e is None:
+            step(i)
+        elif dom == "decode_stream_kernel":
             step(i, None, e)
         elif dom == "prefill_kernel":
             step(i, (None, e[0], e[1], None))
@@ -624,6 +633,7 @@ def main():
         },
         "timing_us": {
             "dominant_kernel_timed": pct(dom_us),
+            "dominant_kernel_samples": f"{len(tev)} of {args.steps} timed steps (every {every}-th)",
             "breakdown_steps": n_prof,
             "append_call": pct(append_us) if n_sep > 0 else None,
             "prefill_call": pct(prefill_us) if pre is not None else None,

@@ -35,9 +35,11 @@
 //    the hardware load counter only has to drain to the stage being
 //    consumed).  Block ids (and the valid token count of each block) are
 //    staged per wave in LDS up front, so no load waits on a block-table read.
-//    Each block's query rows are loaded with its K/V (bf16 path): hardware
-//    load counters drain in issue order, so a query load issued outside the
-//    ring would force the whole ring to land at every switch of segment.
+//    The query rows of a segment are loaded once, during the segment's first
+//    unit for the wave's first segment and during the previous segment's last
+//    unit otherwise, into registers (MFMA A operands); loading them with
+//    every unit instead measured 4.7 us slower on llama3_8b (50% more load
+//    instructions, all L2 hits).
 //  * Scores: bf16 on the matrix cores (Q, GP heads padded to 16 rows, times
 //    K^T of the block's 16 tokens); fp32 by FMA dot products summed over the 8
 //    lanes of a token group by three DPP adds.  Online softmax in the log2
@@ -53,10 +55,13 @@
 //    in the workspace (slot 0: the wave's first segment, slot 1: its last) and
 //    the wave holding its first unit notes it; decode_fixup_kernel then merges
 //    the records of each noted segment (log-sum-exp).  Merging in a second
-//    kernel costs a launch.  Merging in place (coherent record stores and an
-//    arrival counter per segment, the last wave to arrive merging) measured
-//    slower: a segment's first part is the last thing its wave streams, so
-//    nearly every wave would end with the merge's dependent memory round trips.
+//    kernel costs a launch and the gap before it.  Merging in place (records
+//    stored at agent scope, an arrival counter per segment, the last part to
+//    arrive merging) measured slower on llama3_8b (88.9-92 us against 81.4 us
+//    here, with the merge kernel on top: 85-86.6 us per step): 41% of the
+//    wave groups hold a part strictly inside one long segment, which ends
+//    with the wave's stream, so the store, the arrival and the record loads
+//    are round trips after the last unit of the call either way.
 //  * Finished segments wait in LDS and are written after the wave's last load:
 //    a store in mid-stream would hold up the completion count of the loads
 //    issued after it.
@@ -242,6 +247,17 @@ __device__ __forceinline__ void pv_block(float (&acc)[GP][KDPL], float (&l)[GP],
             }
         }
     }
+}
+
+// A register copy the compiler cannot fold away: the result never shares a
+// register with its source, so the source registers are free once it has run.
+__device__ __forceinline__ uint4 opaque_copy(uint4 x) {
+    uint4 y;
+    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.x) : "v"(x.x));
+    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.y) : "v"(x.y));
+    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.z) : "v"(x.z));
+    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.w) : "v"(x.w));
+    return y;
 }
 
 // Pins values in VGPRs at this point in program order: whatever computes them
@@ -605,7 +621,24 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 
     uint32_t qb[GP][kQb], qnb[GP][kQb];
     float qf[GP][kDpl], qnf[GP][kDpl];
-    if constexpr (!kMfma) load_q<T, D, GP, kDpl, kQb>(qb, qf, a, cs, kvg, dl);
+    // MFMA path: the A operands (query rows of the head group, padded to 16
+    // rows) of the current segment, and of the next one, loaded during the last
+    // unit of the current segment
+    uint4 qm[kMf], qmn[kMf];
+    auto load_qm = [&](uint4 (&dst)[kMf], int seq) __attribute__((always_inline)) {
+        const uint32_t hi = mtok < nvh ? (uint32_t)mtok : 0u;
+        const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)seq * a.num_q_heads + h0 + hi) * D;
+#pragma unroll
+        for (int mm = 0; mm < kMf; ++mm) {
+            const int qoff = KV8 ? 64 * (mm / 2) + 16 * mrow + 8 * (mm % 2) : 8 * mrow + 32 * mm;
+            dst[mm] = *reinterpret_cast<const uint4*>(qp + qoff);
+        }
+    };
+    if constexpr (kMfma) {
+        load_qm(qm, cs);
+    } else {
+        load_q<T, D, GP, kDpl, kQb>(qb, qf, a, cs, kvg, dl);
+    }
 
     float m[GP], l[GP], acc[GP][kDpl];
     float mlane[4];  // MFMA layout: running max of the heads of this lane's rows
@@ -620,7 +653,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
 
     uint4 kr[STAGES][2][kVecs], vr[STAGES][2][kVecs];
-    uint4 kb4[STAGES][kMf], qs[STAGES][kMf];
+    uint4 kb4[STAGES][kMf];
     int vld[STAGES];
 
     auto issue = [&](int st, uint4 e) {
@@ -659,16 +692,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             } else {
 #pragma unroll
                 for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = ldg_nt(kb + 32 * mm);
-            }
-            // the unit's query rows travel with its K/V: no load outside the ring
-            // ever has to be waited for (loads complete in issue order)
-            const uint32_t qrow0 = __builtin_amdgcn_readfirstlane(e.z);
-            const uint32_t hi = mtok < nvh ? (uint32_t)mtok : 0u;
-            const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)(qrow0 + hi) * D;
-#pragma unroll
-            for (int mm = 0; mm < kMf; ++mm) {
-                const int qoff = KV8 ? 64 * (mm / 2) + 16 * mrow + 8 * (mm % 2) : 8 * mrow + 32 * mm;
-                qs[st][mm] = *reinterpret_cast<const uint4*>(qp + qoff);
             }
         } else {
 #pragma unroll
@@ -750,12 +773,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             const int blk = u - pref[s];
             const int b = a.block_tables[(size_t)s * a.max_blocks_per_seq + blk];
             const int valid = min(kBlockTokens, a.context_lens[s] - blk * kBlockTokens);
-            // block id; kv head | valid tokens << 16; first query row of the
-            // head group; input row of the new token if this block holds it
-            // (fused append), else ~0
+            // block id; kv head | valid tokens << 16; (unused); input row of
+            // the new token if this block holds it (fused append), else ~0
             const bool holds_new = a.new_k != nullptr && blk == pref[s + 1] - pref[s] - 1;
-            tab[i] = make_uint4((uint32_t)b, (uint32_t)hk | ((uint32_t)valid << 16),
-                                (uint32_t)(s * a.num_q_heads + h0),
+            tab[i] = make_uint4((uint32_t)b, (uint32_t)hk | ((uint32_t)valid << 16), 0u,
                                 holds_new ? (uint32_t)(s * a.num_kv_heads + hk) : 0xFFFFFFFFu);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -783,20 +804,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                 if (has_next) {
                     ++ns;
                     while (pref[ns + 1] == pref[ns]) ++ns;
-                    if constexpr (!kMfma) load_q<T, D, GP, kDpl, kQb>(qnb, qnf, a, ns, kvg, dl);
+                    if constexpr (kMfma) {
+                        load_qm(qmn, ns);
+                    } else {
+                        load_q<T, D, GP, kDpl, kQb>(qnb, qnf, a, ns, kvg, dl);
+                    }
                 }
 
                 const int valid = vld[st];
-                if (valid < kBlockTokens) {
-                    // stale slots past the context: zero their V (may hold NaN)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        if (tg + 8 * t >= valid) {
-#pragma unroll
-                            for (int c = 0; c < kVecs; ++c) vr[st][t][c] = make_uint4(0, 0, 0, 0);
-                        }
-                    }
-                }
                 if constexpr (kMfma) {
                     // ---- scores: S[head][token] = Q K^T on the matrix cores
                     f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
@@ -804,12 +819,36 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 #pragma unroll
                         for (int p = 0; p < kMf / 2; ++p) {
                             const uint4 r = kb4[st][p];
-                            s4 = mfma16x16x32_bf16(qs[st][2 * p], fp8x8_to_bf16x8(r.x, r.y), s4);
-                            s4 = mfma16x16x32_bf16(qs[st][2 * p + 1], fp8x8_to_bf16x8(r.z, r.w), s4);
+                            s4 = mfma16x16x32_bf16(qm[2 * p], fp8x8_to_bf16x8(r.x, r.y), s4);
+                            s4 = mfma16x16x32_bf16(qm[2 * p + 1], fp8x8_to_bf16x8(r.z, r.w), s4);
                         }
                     } else {
 #pragma unroll
-                        for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qs[st][mm], kb4[st][mm], s4);
+                        for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qm[mm], kb4[st][mm], s4);
+                    }
+                    // V leaves the ring for working registers, and the stage is
+                    // refilled at once: the loads of unit ux + STAGES then run
+                    // during this unit's softmax and P*V instead of after them.
+                    uint4 vw[2][kVecs];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                        for (int c = 0; c < kVecs; ++c) vw[t][c] = opaque_copy(vr[st][t][c]);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(s4[r]));
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue(st, e_refill);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (valid < kBlockTokens) {
+                        // stale slots past the context: zero their V (may hold NaN)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            if (tg + 8 * t >= valid) {
+#pragma unroll
+                                for (int c = 0; c < kVecs; ++c) vw[t][c] = make_uint4(0, 0, 0, 0);
+                            }
+                        }
                     }
                     float sv[4];
                     bool need = false;
@@ -864,11 +903,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                         }
                     }
                     if constexpr (KV8) {
-                        pv_block_fp8<GP, kDpl>(acc, l, pk, vr[st]);
+                        pv_block_fp8<GP, kDpl>(acc, l, pk, vw);
                     } else {
-                        pv_block_packed<GP, kDpl, kVecs>(acc, l, pk, vr[st]);
+                        pv_block_packed<GP, kDpl, kVecs>(acc, l, pk, vw);
                     }
                 } else {
+                    if (valid < kBlockTokens) {
+                        // stale slots past the context: zero their V (may hold NaN)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            if (tg + 8 * t >= valid) {
+#pragma unroll
+                                for (int c = 0; c < kVecs; ++c) vr[st][t][c] = make_uint4(0, 0, 0, 0);
+                            }
+                        }
+                    }
                     // ---- scores of this block
                     float sc[2][GP];
                     qk_block<T, GP, kDpl, kVecs, kQb>(sc, kr[st], qb, qf);
@@ -900,14 +949,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                         for (int g = 0; g < GP; ++g) p[t][g] = fast_exp2(sc[t][g] - m[g]);
                     }
                     pv_block<T, GP, kDpl, kVecs>(acc, l, p, vr[st]);
+                    // ---- refill this stage (unconditionally, see above), once
+                    // its registers are no longer read
+                    keep_in_regs<GP, kDpl>(acc, l);
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue(st, e_refill);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-
-                // ---- refill this stage (unconditionally, see above), once its
-                // registers are no longer read
-                keep_in_regs<GP, kDpl>(acc, l);
-                __builtin_amdgcn_sched_barrier(0);
-                issue(st, e_refill);
-                __builtin_amdgcn_sched_barrier(0);
 
                 if (!seg_end) {
                     ++cblk;
@@ -919,7 +967,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                     cblk = 0;
                     cnb = pref[cs + 1] - pref[cs];
                     seg_first_blk = 0;
-                    if constexpr (!kMfma) {
+                    if constexpr (kMfma) {
+#pragma unroll
+                        for (int mm = 0; mm < kMf; ++mm) qm[mm] = qmn[mm];
+                    } else {
 #pragma unroll
                         for (int g = 0; g < GP; ++g) {
 #pragma unroll

@@ -133,8 +133,18 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
     }
     // Scores are scaled inside the exponent, exp2(s * scale - m), with the
     // running max taken over raw scores; for a negative scale q is negated
-    // (exact in bf16) so that the scale used is positive.
-    const float qscale = fabsf(a.scale_log2);
+    // (exact in bf16) so that the scale used is positive.  A zero scale makes
+    // every score 0: q is zeroed and the scale set to 1 instead, so that the
+    // masked scores (-inf) are not multiplied by 0.
+    const bool zero_scale = a.scale_log2 == 0.f;
+    const float qscale = zero_scale ? 1.f : fabsf(a.scale_log2);
+    if (zero_scale) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+            for (int m = 0; m < kMs; ++m) qb[ct][m] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
     if (a.scale_log2 < 0.f) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {

@@ -106,7 +106,7 @@ def test_continuous_batching_replay():
         q, kn, vn = _bf16(rng, (s, hq, d)), _bf16(rng, (s, hkv, d)), _bf16(rng, (s, hkv, d))
         out = torch.empty((s, hq, d), dtype=torch.bfloat16, device="cuda")
         if ws is None or ws.numel() < ops.decode_workspace_size(s, hq, hkv, d, mb):
-            ws = torch.empty(ops.decode_workspace_size(max(s, 64), hq, hkv, d, mb), dtype=torch.uint8,
+            ws = torch.zeros(ops.decode_workspace_size(max(s, 64), hq, hkv, d, mb), dtype=torch.uint8,
                              device="cuda")
         print(f"[gpu] replay step {step}: S={s} copies={len(copies)} free={cpp.num_free}", flush=True)
         ops.decode_append(out, to_dev(q), to_dev(kn), to_dev(vn), dk, dv, to_dev(bt), to_dev(cl), scale,
