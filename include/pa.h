@@ -190,6 +190,30 @@ int pa_decode_append(void *out, const void *q, const void *key, const void *valu
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_append without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing.  The records of
+ * contexts split across waves go to a fixed 16 MiB array that the library holds
+ * on each device it runs on until the process ends.  A call needs
+ * waves * 2 * h * (head_dim + 2) * 4 bytes of it plus 16 bytes per wave, where
+ * h is the query heads per wave (the query heads per kv head rounded up to a
+ * power of two, at most 8) and waves is 1024 on MI355X unless
+ * pa_decode_set_launch chose another count: every supported shape fits at
+ * 1024 waves; PA_EWORKSPACE for a call that does not fit (nothing is launched).
+ * Every call on one device uses that device's array, so calls that may overlap
+ * in time on one device race: enqueue them on one stream.  The array needs no
+ * clearing (every record a call reads is written earlier in the same call).
+ * Otherwise identical to pa_decode_append.
+ */
+int pa_decode_append_noalloc(void *out, const void *q, const void *key, const void *value,
+                             void *k_cache, void *v_cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                             void *stream);
+
+/*
  * pa_decode over fp8 caches (written by pa_reshape_and_cache_fp8): what
  * pa_decode computes with K_t and V_t the dequantized rows k_scale * e4m3(.)
  * and v_scale * e4m3(.).  q and out are bf16 (dtype must be PA_BF16, else

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_launch.h"
@@ -66,11 +67,12 @@ struct DecodeWsLayout {
     size_t split, ml, acc, total;
 };
 
-DecodeWsLayout decode_ws_layout(int gp, int32_t head_dim) {
+// waves: the records of this many waves (every launch shape, by default).
+DecodeWsLayout decode_ws_layout(int gp, int32_t head_dim, int waves = pa::kDecodeMaxWaves) {
     DecodeWsLayout L;
-    const size_t recs = (size_t)pa::kDecodeMaxWaves * 2 * gp;
+    const size_t recs = (size_t)waves * 2 * gp;
     L.split = 0;
-    L.ml = L.split + align256((size_t)pa::kDecodeMaxWaves * sizeof(pa::SplitNote));
+    L.ml = L.split + align256((size_t)waves * sizeof(pa::SplitNote));
     L.acc = L.ml + align256(recs * 2 * sizeof(float));
     L.total = L.acc + align256(recs * head_dim * sizeof(float));
     return L;
@@ -104,6 +106,34 @@ int decode_waves(int per_cu) {
     w = (w / pa::kDecodeWaves) * pa::kDecodeWaves;
     if (w < pa::kDecodeWaves) w = pa::kDecodeWaves;
     return (int)w;
+}
+
+// Decode records for pa_decode_append_noalloc: a fixed array on each device
+// that the library keeps until the process ends (each device holds its own
+// copy at its own address).  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of this device's scratch, or nullptr if the runtime refuses
+// the lookup.
+void* scratch_address() {
+    static std::atomic<void*> addr[64];
+    static std::mutex lock;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> guard(lock);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+        addr[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
 }
 
 }  // namespace
@@ -221,7 +251,7 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                 int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
                 void* workspace, size_t workspace_bytes, void* stream, void* kernel_start, void* kernel_stop,
-                bool fused, bool launch = true, const KvScales* kv8 = nullptr) {
+                bool fused, bool launch = true, const KvScales* kv8 = nullptr, bool static_scratch = false) {
     int rc = check_dtype(dtype);
     if (rc) return rc;
     if (kv8) {
@@ -242,11 +272,30 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     if (num_seqs > pa::kDecodeMaxSeqs) return PA_EUNSUPPORTED;
     const int group = num_q_heads / num_kv_heads;
     const int gp = heads_per_wave(group);
-    const DecodeWsLayout ws = decode_ws_layout(gp, head_dim);
-    if (workspace == nullptr || workspace_bytes < ws.total) return PA_EWORKSPACE;
+    pa::DecodeArgs a;
+    a.groups_per_kv = (group + gp - 1) / gp;
+    a.n_kvg = num_kv_heads * a.groups_per_kv;
+    // wave groups of n_kvg waves (one per head group), as many as fit the
+    // persistent grid and the workspace records
+    const bool two_groups_fit = (head_dim == 64 || gp <= 4) &&
+                                2 * pa::decode_lds_bytes(head_dim, gp, num_seqs) <= pa::kLdsBytesPerCU;
+    const int per_cu = kv8 && two_groups_fit ? pa::kDecodeWavesPerCUFp8 : pa::kDecodeWavesPerCU;
+    a.wave_groups = std::max(1, std::min(decode_waves(per_cu), pa::kDecodeMaxWaves) / a.n_kvg);
+    if ((long long)a.wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
+    a.waves = a.wave_groups * a.n_kvg;
+    // a caller's workspace is laid out for every launch shape; the fixed
+    // scratch for exactly this call's waves, and it must hold them
+    const DecodeWsLayout ws = static_scratch ? decode_ws_layout(gp, head_dim, a.waves) : decode_ws_layout(gp, head_dim);
+    if (static_scratch) {
+        if (ws.total > kNoAllocScratchBytes) return PA_EWORKSPACE;
+        workspace = launch ? scratch_address() : nullptr;
+        workspace_bytes = kNoAllocScratchBytes;
+        if (launch && workspace == nullptr) return PA_ELAUNCH;
+    } else if (workspace == nullptr || workspace_bytes < ws.total) {
+        return PA_EWORKSPACE;
+    }
     if (!launch) return PA_OK;  // arguments checked only
 
-    pa::DecodeArgs a;
     a.out = out;
     a.q = q;
     a.k_cache = k_cache;
@@ -265,16 +314,6 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.group = group;
-    a.groups_per_kv = (group + gp - 1) / gp;
-    a.n_kvg = num_kv_heads * a.groups_per_kv;
-    // wave groups of n_kvg waves (one per head group), as many as fit the
-    // persistent grid and the workspace records
-    const bool two_groups_fit = (head_dim == 64 || gp <= 4) &&
-                                2 * pa::decode_lds_bytes(head_dim, gp, num_seqs) <= pa::kLdsBytesPerCU;
-    const int per_cu = kv8 && two_groups_fit ? pa::kDecodeWavesPerCUFp8 : pa::kDecodeWavesPerCU;
-    a.wave_groups = std::max(1, std::min(decode_waves(per_cu), pa::kDecodeMaxWaves) / a.n_kvg);
-    if ((long long)a.wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
-    a.waves = a.wave_groups * a.n_kvg;
     a.unit_ticks = pa::kDecodeUnitTicks;
     const int ov_ticks = g_override_switch_ticks.load(std::memory_order_relaxed);
     a.switch_ticks = ov_ticks >= 0 ? ov_ticks : pa::kDecodeSwitchTicks;
@@ -354,6 +393,16 @@ int pa_decode_append_timed(void* out, const void* q, const void* key, const void
     return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                        workspace, workspace_bytes, stream, kernel_start, kernel_stop, true);
+}
+
+int pa_decode_append_noalloc(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                             void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float scale, pa_dtype dtype, void* stream) {
+    return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                       nullptr, 0, stream, nullptr, nullptr, true, true, nullptr, true);
 }
 
 int pa_decode_append_graph(void** graph_exec, void* out, const void* q, const void* key, const void* value,

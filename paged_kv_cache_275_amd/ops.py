@@ -66,6 +66,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_append_timed.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
                                            ctypes.c_int, p, sz, p, p, p]
     lib.pa_decode_append_timed.restype = ctypes.c_int
+    lib.pa_decode_append_noalloc.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32,
+                                             ctypes.c_int, p]
+    lib.pa_decode_append_noalloc.restype = ctypes.c_int
     lib.pa_decode_append_graph.argtypes = [ctypes.POINTER(p), p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32,
                                            i32, i64, f32, ctypes.c_int, p, sz]
     lib.pa_decode_append_graph.restype = ctypes.c_int
@@ -383,6 +386,36 @@ def bind_decode_append(out, q, key, value, k_cache, v_cache, block_tables, conte
         else:
             _check(lib, "pa_decode_append_timed", timed(*args, *kernel_events))
     return call
+
+
+def decode_append_noalloc(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                          stream=None) -> None:
+    """pa_decode_append_noalloc: the fused decode step with the library's fixed
+    per-device scratch instead of a workspace (nothing is allocated)."""
+    lib = load_library()
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, _NO_WORKSPACE, stream)
+    _need(key, "key", q.dtype, 3)
+    _need(value, "value", q.dtype, 3)
+    if tuple(key.shape) != (q.shape[0], k_cache.shape[2], q.shape[2]) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    args = args[:2] + (key.data_ptr(), value.data_ptr()) + args[2:15] + (args[17],)
+    _check(lib, "pa_decode_append_noalloc", lib.pa_decode_append_noalloc(*args))
+
+
+class _NoWorkspace:
+    """Stands in for a workspace tensor where none is passed (no allocation)."""
+
+    def data_ptr(self):
+        return 0
+
+    def numel(self):
+        return 0
+
+    def element_size(self):
+        return 1
+
+
+_NO_WORKSPACE = _NoWorkspace()
 
 
 class DecodeStepGraph:
