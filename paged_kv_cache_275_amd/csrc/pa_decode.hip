@@ -350,23 +350,6 @@ __device__ __forceinline__ void store_run(OutT* dst, const float (&v)[CH], float
     }
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave: row_shr 1, 2, 4, 8 within
-// each 16-lane row, then row 0's total into row 1 and row 2's into row 3
-// (row_bcast:15), then the first two rows' total into rows 2 and 3
-// (row_bcast:31).  Lanes without a source read 0.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ int dpp_src_i32(int x) {
-    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWMASK, 0xF, true);
-}
-__device__ __forceinline__ int wave_scan_incl(int x) {
-    x += dpp_src_i32<0x111, 0xF>(x);
-    x += dpp_src_i32<0x112, 0xF>(x);
-    x += dpp_src_i32<0x114, 0xF>(x);
-    x += dpp_src_i32<0x118, 0xF>(x);
-    x += dpp_src_i32<0x142, 0xA>(x);
-    x += dpp_src_i32<0x143, 0xC>(x);
-    return x;
-}
 
 // Work is measured in TICKS: every unit costs unit_ticks, and every segment
 // adds switch_ticks for the work of closing it (reduction, stores, a fresh

@@ -83,6 +83,24 @@ __device__ __forceinline__ float readlane_f32(float x, int lane) {
 // D[16x16] += A[16x32] * B[32x16] in bf16 with fp32 accumulation.  Lane l holds
 // A row l%16 and B column l%16, k-slots 8*(l/16) .. +8 (8 bf16 in 16 bytes);
 // it receives D column l%16, rows 4*(l/16) .. +3.
+// Inclusive prefix sum over the 64 lanes of a wave: row_shr 1, 2, 4, 8 within
+// each 16-lane row, then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then the first two rows' total into rows 2 and 3
+// (row_bcast:31).  Lanes without a source read 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_src_i32(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWMASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_scan_incl(int x) {
+    x += dpp_src_i32<0x111, 0xF>(x);
+    x += dpp_src_i32<0x112, 0xF>(x);
+    x += dpp_src_i32<0x114, 0xF>(x);
+    x += dpp_src_i32<0x118, 0xF>(x);
+    x += dpp_src_i32<0x142, 0xA>(x);
+    x += dpp_src_i32<0x143, 0xC>(x);
+    return x;
+}
+
 __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);

@@ -137,6 +137,18 @@ def _run_small(rng, hq, hkv, d, chunks, prefixes, scale):
     assert_attention_close(widen_dev(out), ref, "bf16", f"chunks={chunks} prefixes={prefixes}")
 
 
+@pytest.mark.parametrize("num_seqs", [600, 1100])
+def test_prefill_many_sequences(num_seqs):
+    """More sequences than one workgroup scans at a time (512), with empty
+    chunks among them, so the item lookup crosses batches."""
+    rng = np.random.default_rng(num_seqs)
+    chunks = [int(x) for x in rng.integers(0, 4, num_seqs)]
+    prefixes = [int(x) for x in rng.integers(0, 41, num_seqs)]
+    chunks[-1] = max(chunks[-1], 1)   # the last sequence's items end the grid
+    print(f"[gpu] prefill {num_seqs} sequences, {sum(chunks)} rows", flush=True)
+    _run_small(rng, 4, 2, 64, chunks, prefixes, 0.125)
+
+
 def test_prefill_rejects_fp32():
     q = torch.zeros((4, 4, 64), dtype=torch.float32, device="cuda")
     kc = torch.zeros((2, 16, 2, 64), dtype=torch.float32, device="cuda")
