@@ -20,6 +20,9 @@ kernel's current source, else null.
 Other modes (for the profiling summaries under profiles/):
   --copy-calibration   a plain 512 MiB device copy, to scale HBM counters
   --summarize-pmc ...  turn rocprofv3 counter CSVs into a traffic summary
+  --summarize-stats ...  turn a rocprofv3 --stats CSV and the profiled bench
+                       log into a kernel-time summary
+  --summarize-counters ...  per-dispatch medians and ratios of SQ/GRBM counters
 """
 from __future__ import annotations
 
@@ -428,6 +431,91 @@ def summarize_pmc(args):
     print("\n".join(lines))
 
 
+def summarize_stats(args):
+    """Write profiles/<kernel>_<workload>_kernel_stats.md from a rocprofv3
+    --kernel-trace --stats CSV and the log of the bench run it profiled."""
+    with open(args.stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    with open(args.bench_log) as f:
+        bench = [line.strip() for line in f if line.startswith("{")][-1]
+    b = json.loads(bench)
+    rf = b["roofline"]
+    lines = [f"# {args.kernel} on {args.workload}: rocprofv3 kernel trace", "",
+             "Commands, from the repository root (on one MI355X):", "", "```",
+             *args.commands.split(";;"), "```", "",
+             "Per-kernel summary (rocprofv3 --stats, durations in ns; the calls include the warm-up, "
+             "breakdown and extra passes of bench.py):", "",
+             "| kernel | calls | average ns | min ns | max ns | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("void ", "").split("(")[0]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    # the instance the bench line timed: the bf16-cache (non-fp8) one
+    inst = [r for r in rows if kernel_matches(rf["kernel"], r["Name"]) and "true>" not in r["Name"]]
+    lines.append("")
+    if inst:
+        avg = float(inst[0]["AverageNs"]) / 1e3
+        lines.append(f"The bench line timed `{rf['kernel']}` with HIP events at {rf['avg_us']} us per launch on "
+                     f"average; rocprofv3 gives {avg:.2f} us for `{inst[0]['Name'].replace('void ', '').split('(')[0]}`.")
+    lines += [f"roofline of that line: achieved {rf['achieved']} {rf['unit']} of {rf['peak']} "
+              f"({rf['frac'] * 100:.1f}%).", "", "Bench line of the profiled run:", "", "```", bench, "```", ""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+# Ratios derived from SQ / GRBM counters: (name, numerator, denominator, scale, meaning)
+COUNTER_RATIOS = [
+    ("mfma_busy", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", 0.25,
+     "matrix-core busy cycles per SIMD over CU-busy cycles (4 SIMDs per CU)"),
+    ("lds_bank_conflict", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", 1.0,
+     "LDS cycles stalled by bank conflicts over LDS active cycles"),
+    ("lds_wait_per_lds_inst", "SQ_WAIT_INST_LDS", "SQ_INSTS_LDS", 1.0,
+     "wave cycles waiting to issue an LDS instruction, per LDS instruction"),
+    ("mfma_flops_per_mops", None, None, 512.0, "one MFMA MOP is 512 flops (bf16)"),
+]
+
+
+def summarize_counters(args):
+    """Write profiles/<kernel>_<workload>_counters.md: per-dispatch medians of
+    rocprofv3 --pmc counters for one kernel (several CSVs, one per pass)."""
+    import statistics
+    med = {}
+    n_disp = {}
+    for path in args.counter_csvs.split(","):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel_matches(args.kernel, r["Kernel_Name"]) and "true>" not in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for k, v in vals.items():
+            med[k] = statistics.median(v)
+            n_disp[k] = len(v)
+    if not med:
+        raise SystemExit(f"no {args.kernel} dispatches in the counter files")
+    lines = [f"# {args.kernel} on {args.workload}: hardware counters (rocprofv3 --pmc)", "",
+             "Commands, from the repository root (on one MI355X; one counter pass per command):", "", "```",
+             *args.commands.split(";;"), "```", "",
+             "Median per dispatch of the bf16-cache instance (counters summed over the device):", "",
+             "| counter | dispatches | median |", "|---|---|---|"]
+    for k in sorted(med):
+        lines.append(f"| {k} | {n_disp[k]} | {med[k]:.0f} |")
+    lines += ["", "| ratio | value | definition |", "|---|---|---|"]
+    for name, num, den, scale, meaning in COUNTER_RATIOS:
+        if num and num in med and den in med and med[den] > 0:
+            lines.append(f"| {name} | {med[num] / med[den] * scale:.3f} | {num} / {den}"
+                         f"{'' if scale == 1.0 else f' x {scale:g}'}: {meaning} |")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+        fl = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+        extra = f"; algorithmic {args.algorithmic_flops:.4g}, ratio {fl / args.algorithmic_flops:.3f}" \
+            if args.algorithmic_flops else ""
+        lines.append(f"| mfma_flops | {fl:.4g} | SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512{extra} |")
+    lines.append("")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -452,6 +540,12 @@ def main():
     ap.add_argument("--algorithmic-bytes", type=int, default=0)
     ap.add_argument("--commands", default="")
     ap.add_argument("--out")
+    ap.add_argument("--summarize-stats", action="store_true")
+    ap.add_argument("--stats-csv")
+    ap.add_argument("--bench-log")
+    ap.add_argument("--summarize-counters", action="store_true")
+    ap.add_argument("--counter-csvs", default="")
+    ap.add_argument("--algorithmic-flops", type=float, default=0.0)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -460,6 +554,12 @@ def main():
         sys.exit(2)
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_stats:
+        summarize_stats(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
         return
     if args.copy_calibration:
         copy_calibration()
