@@ -285,7 +285,43 @@ int pa_decode_append_graph(void **graph_exec, void *out, const void *q, const vo
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
                            void *workspace, size_t workspace_bytes);
-/* Enqueue a graph from pa_decode_append_graph on stream (NULL = default). */
+
+/*
+ * The decode step over fp8 caches: sequence s's new K/V row (row s of key and
+ * value, bf16 [num_seqs, num_kv_heads, head_dim]) is quantized into the caches
+ * at position n-1 = context_lens[s]-1 exactly as pa_reshape_and_cache_fp8 does
+ * (e4m3 of x / scale, nearest even, saturated at +-448), then pa_decode_fp8
+ * runs over all n tokens.  Three kernel launches: the quantized append first
+ * (the fp8 streaming kernel reads every token from the cache; it cannot take
+ * the new rows from the inputs as pa_decode_append does, because their bytes
+ * exist only after quantization), then the two of pa_decode_fp8.  Sequences
+ * with n = 0 append nothing and get zero rows.  Arguments, workspace and errors
+ * as pa_decode_fp8; key/value must be non-NULL (PA_EINVAL otherwise) and must
+ * not overlap the caches.
+ */
+int pa_decode_append_fp8(void *out, const void *q, const void *key, const void *value,
+                         void *k_cache, void *v_cache,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq,
+                         const int32_t *context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, float scale,
+                         float k_scale, float v_scale, pa_dtype dtype,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_append_fp8 recorded as a HIP graph, as pa_decode_append_graph
+ * records pa_decode_append (the scales are baked in with the pointers).
+ */
+int pa_decode_append_fp8_graph(void **graph_exec, void *out, const void *q, const void *key,
+                               const void *value, void *k_cache, void *v_cache,
+                               const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, float scale,
+                               float k_scale, float v_scale, pa_dtype dtype,
+                               void *workspace, size_t workspace_bytes);
+/* Enqueue a graph from pa_decode_append_graph or pa_decode_append_fp8_graph on
+ * stream (NULL = default). */
 int pa_graph_launch(void *graph_exec, void *stream);
 /* Release a graph instance (NULL is a no-op). */
 int pa_graph_destroy(void *graph_exec);

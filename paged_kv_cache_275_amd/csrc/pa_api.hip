@@ -245,7 +245,9 @@ struct KvScales {
 
 // pa_decode and its fused-append, fp8-cache and timed variants: key/value
 // non-null means fused append (the caches are then written); kv8 non-null
-// means the caches hold FP8 E4M3 (q and out bf16).
+// means the caches hold FP8 E4M3 (q and out bf16).  With both, the new rows
+// are quantized into the cache by a kernel of their own before the decode
+// kernels, which then read every token from the cache.
 int decode_impl(void* out, const void* q, const void* key, const void* value, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -255,7 +257,7 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     int rc = check_dtype(dtype);
     if (rc) return rc;
     if (kv8) {
-        if (dtype != PA_BF16 || fused) return PA_EUNSUPPORTED;
+        if (dtype != PA_BF16) return PA_EUNSUPPORTED;
         rc = check_kv_scales(kv8->k, kv8->v);
         if (rc) return rc;
     }
@@ -302,6 +304,14 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
+    if (fused && kv8) {
+        const hipError_t e = pa::launch_append_rows_fp8(key, value, const_cast<void*>(k_cache),
+                                                        const_cast<void*>(v_cache), block_tables, max_blocks_per_seq,
+                                                        context_lens, num_seqs, num_kv_heads * head_dim,
+                                                        1.0f / kv8->k, 1.0f / kv8->v, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return PA_ELAUNCH;
+        fused = false;  // the decode kernels read the new token from the cache
+    }
     a.new_k = fused ? key : nullptr;
     a.new_v = fused ? value : nullptr;
     a.k_cache_w = fused ? const_cast<void*>(k_cache) : nullptr;
@@ -405,20 +415,23 @@ int pa_decode_append_noalloc(void* out, const void* q, const void* key, const vo
                        nullptr, 0, stream, nullptr, nullptr, true, true, nullptr, true);
 }
 
-int pa_decode_append_graph(void** graph_exec, void* out, const void* q, const void* key, const void* value,
-                           void* k_cache, void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                           float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes) {
+namespace {
+
+// pa_decode_append_graph and its fp8 variant (kv8 non-null): the step's
+// launches recorded on a private stream (default priority) in capture mode,
+// then instantiated.
+int append_graph_impl(void** graph_exec, void* out, const void* q, const void* key, const void* value,
+                      void* k_cache, void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                      void* workspace, size_t workspace_bytes, const KvScales* kv8) {
     if (!graph_exec) return PA_EINVAL;
     *graph_exec = nullptr;
     if (num_seqs <= 0) return PA_EINVAL;  // an empty graph is of no use
     int rc = decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
-                         workspace, workspace_bytes, nullptr, nullptr, nullptr, true, false);
+                         workspace, workspace_bytes, nullptr, nullptr, nullptr, true, false, kv8);
     if (rc != PA_OK) return rc;
-    // Record the launches on a private stream (default priority) in capture
-    // mode, then instantiate.
     hipStream_t cs = nullptr;
     if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return PA_ELAUNCH;
     rc = PA_ELAUNCH;
@@ -426,7 +439,7 @@ int pa_decode_append_graph(void** graph_exec, void* out, const void* q, const vo
     if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess) {
         rc = decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
-                         workspace, workspace_bytes, cs, nullptr, nullptr, true);
+                         workspace, workspace_bytes, cs, nullptr, nullptr, true, true, kv8);
         const hipError_t e = hipStreamEndCapture(cs, &graph);
         if (rc == PA_OK && e != hipSuccess) rc = PA_ELAUNCH;
     }
@@ -441,6 +454,41 @@ int pa_decode_append_graph(void** graph_exec, void* out, const void* q, const vo
     if (graph) (void)hipGraphDestroy(graph);
     (void)hipStreamDestroy(cs);
     return rc;
+}
+
+}  // namespace
+
+int pa_decode_append_graph(void** graph_exec, void* out, const void* q, const void* key, const void* value,
+                           void* k_cache, void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes) {
+    return append_graph_impl(graph_exec, out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                             context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             scale, dtype, workspace, workspace_bytes, nullptr);
+}
+
+int pa_decode_append_fp8(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, float k_scale,
+                         float v_scale, pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    const KvScales kv{k_scale, v_scale};
+    return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, workspace,
+                       workspace_bytes, stream, nullptr, nullptr, true, true, &kv);
+}
+
+int pa_decode_append_fp8_graph(void** graph_exec, void* out, const void* q, const void* key, const void* value,
+                               void* k_cache, void* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, float scale, float k_scale, float v_scale, pa_dtype dtype,
+                               void* workspace, size_t workspace_bytes) {
+    const KvScales kv{k_scale, v_scale};
+    return append_graph_impl(graph_exec, out, q, key, value, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                             context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             scale, dtype, workspace, workspace_bytes, &kv);
 }
 
 int pa_graph_launch(void* graph_exec, void* stream) {

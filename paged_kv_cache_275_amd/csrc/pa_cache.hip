@@ -45,9 +45,37 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
     return hipGetLastError();
 }
 
-// KV append into an FP8 E4M3 cache: every element becomes
-// e4m3(clamp(x * inv_scale, +-448)), nearest even (x * inv_scale in fp32).
-// Each thread turns 16 elements of one K or V row into 16 bytes.
+// One 16-element piece of a K or V row as 16 E4M3 bytes: every element
+// becomes e4m3(clamp(x * inv_scale, +-448)), nearest even (x * inv_scale in
+// fp32).
+template <typename T>
+__device__ __forceinline__ uint4 fp8_piece16(const T* src, float inv) {
+    float x[16];
+    if constexpr (sizeof(T) == 2) {
+        const uint4 u0 = reinterpret_cast<const uint4*>(src)[0];
+        const uint4 u1 = reinterpret_cast<const uint4*>(src)[1];
+        const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            x[2 * k] = bf16_lo(w[k]) * inv;
+            x[2 * k + 1] = bf16_hi(w[k]) * inv;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 f = reinterpret_cast<const float4*>(src)[k];
+            x[4 * k] = f.x * inv;
+            x[4 * k + 1] = f.y * inv;
+            x[4 * k + 2] = f.z * inv;
+            x[4 * k + 3] = f.w * inv;
+        }
+    }
+    return make_uint4(pack_fp8x4(x[0], x[1], x[2], x[3]), pack_fp8x4(x[4], x[5], x[6], x[7]),
+                      pack_fp8x4(x[8], x[9], x[10], x[11]), pack_fp8x4(x[12], x[13], x[14], x[15]));
+}
+
+// KV append into an FP8 E4M3 cache (fp8_piece16 per 16 elements).  Each
+// thread turns 16 elements of one K or V row into 16 bytes.
 template <typename T>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const T* __restrict__ key, const T* __restrict__ value, uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
@@ -61,32 +89,46 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
         const int vec = (int)(j % row_vecs);
         const int slot = slot_mapping[tok];
         if (slot < 0) continue;
-        const T* src = (is_v ? value : key) + j * 16;
-        const float inv = is_v ? v_inv : k_inv;
-        float x[16];
-        if constexpr (sizeof(T) == 2) {
-            const uint4 u0 = reinterpret_cast<const uint4*>(src)[0];
-            const uint4 u1 = reinterpret_cast<const uint4*>(src)[1];
-            const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                x[2 * k] = bf16_lo(w[k]) * inv;
-                x[2 * k + 1] = bf16_hi(w[k]) * inv;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 f = reinterpret_cast<const float4*>(src)[k];
-                x[4 * k] = f.x * inv;
-                x[4 * k + 1] = f.y * inv;
-                x[4 * k + 2] = f.z * inv;
-                x[4 * k + 3] = f.w * inv;
-            }
-        }
-        const uint4 o = make_uint4(pack_fp8x4(x[0], x[1], x[2], x[3]), pack_fp8x4(x[4], x[5], x[6], x[7]),
-                                   pack_fp8x4(x[8], x[9], x[10], x[11]), pack_fp8x4(x[12], x[13], x[14], x[15]));
+        const uint4 o = fp8_piece16((is_v ? value : key) + j * 16, is_v ? v_inv : k_inv);
         (is_v ? v_cache : k_cache)[(long long)slot * row_vecs + vec] = o;
     }
+}
+
+// The decode step's append into an FP8 cache: sequence s's new K/V row
+// (row s of key / value) goes to position context_lens[s] - 1, its slot
+// found through the block table; sequences with no tokens are skipped.
+__global__ __launch_bounds__(256) void append_rows_fp8_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache, const int32_t* __restrict__ block_tables, int max_blocks_per_seq,
+    const int32_t* __restrict__ context_lens, int num_seqs, int row_vecs, float k_inv, float v_inv) {
+    const long long per_tensor = (long long)num_seqs * row_vecs;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * per_tensor;
+         i += (long long)gridDim.x * blockDim.x) {
+        const bool is_v = i >= per_tensor;
+        const long long j = is_v ? i - per_tensor : i;
+        const int sq = (int)(j / row_vecs);
+        const int vec = (int)(j % row_vecs);
+        const int n = context_lens[sq];
+        if (n <= 0) continue;
+        const long long slot = (long long)block_tables[(size_t)sq * max_blocks_per_seq + (n - 1) / kBlockTokens] *
+                                   kBlockTokens + (n - 1) % kBlockTokens;
+        const uint4 o = fp8_piece16((is_v ? value : key) + j * 16, is_v ? v_inv : k_inv);
+        (is_v ? v_cache : k_cache)[slot * row_vecs + vec] = o;
+    }
+}
+
+hipError_t launch_append_rows_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int row_elems, float k_inv, float v_inv, hipStream_t stream) {
+    const int row_vecs = row_elems / 16;
+    const long long total = 2LL * num_seqs * row_vecs;
+    long long blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(append_rows_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, row_vecs, k_inv, v_inv);
+    return hipGetLastError();
 }
 
 hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,

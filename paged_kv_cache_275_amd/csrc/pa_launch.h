@@ -106,6 +106,11 @@ size_t decode_lds_bytes(int head_dim, int gp, int num_seqs);
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages, bool kv8,
                          hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// The decode step's new rows (bf16 [num_seqs, row_elems]) quantized into an
+// FP8 cache at each sequence's last position, slots through the block table.
+hipError_t launch_append_rows_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int row_elems, float k_inv, float v_inv, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int num_tokens, int row_bytes,
                                     hipStream_t stream);

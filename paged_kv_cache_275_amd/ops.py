@@ -72,6 +72,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_append_graph.argtypes = [ctypes.POINTER(p), p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32,
                                            i32, i64, f32, ctypes.c_int, p, sz]
     lib.pa_decode_append_graph.restype = ctypes.c_int
+    lib.pa_decode_append_fp8.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i64, f32, f32, f32,
+                                         ctypes.c_int, p, sz, p]
+    lib.pa_decode_append_fp8.restype = ctypes.c_int
+    lib.pa_decode_append_fp8_graph.argtypes = [ctypes.POINTER(p), p, p, p, p, p, p, p, i32, p, i32, i32, i32,
+                                               i32, i32, i64, f32, f32, f32, ctypes.c_int, p, sz]
+    lib.pa_decode_append_fp8_graph.restype = ctypes.c_int
     lib.pa_graph_launch.argtypes = [p, p]
     lib.pa_graph_launch.restype = ctypes.c_int
     lib.pa_graph_destroy.argtypes = [p]
@@ -402,6 +408,43 @@ def decode_append_noalloc(out, q, key, value, k_cache, v_cache, block_tables, co
     _check(lib, "pa_decode_append_noalloc", lib.pa_decode_append_noalloc(*args))
 
 
+def _decode_append_fp8_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                            v_scale, workspace, stream) -> tuple:
+    import torch
+    args, ws = _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                                workspace, stream)
+    _need(key, "key", torch.bfloat16, 3)
+    _need(value, "value", torch.bfloat16, 3)
+    if tuple(key.shape) != (q.shape[0], k_cache.shape[2], q.shape[2]) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    return args[:2] + (key.data_ptr(), value.data_ptr()) + args[2:], ws
+
+
+def decode_append_fp8(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      k_scale: float, v_scale: float, workspace=None, stream=None) -> None:
+    """Decode step over fp8 caches (pa_decode_append_fp8): key/value bf16
+    [S, Hkv, D], each sequence's new token, quantized into the caches at
+    position context_lens[s] - 1, then attention over all tokens."""
+    lib = load_library()
+    args, _ = _decode_append_fp8_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale,
+                                      k_scale, v_scale, workspace, stream)
+    _check(lib, "pa_decode_append_fp8", lib.pa_decode_append_fp8(*args))
+
+
+def bind_decode_append_fp8(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                           k_scale: float, v_scale: float, workspace=None, stream=None):
+    """Check the arguments once; return f() that enqueues the same fp8 decode
+    step again (see bind_reshape_and_cache)."""
+    lib = load_library()
+    args, ws = _decode_append_fp8_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale,
+                                       k_scale, v_scale, workspace, stream)
+    fn = lib.pa_decode_append_fp8
+
+    def call(_keep=ws):
+        _check(lib, "pa_decode_append_fp8", fn(*args))
+    return call
+
+
 class _NoWorkspace:
     """Stands in for a workspace tensor where none is passed (no allocation)."""
 
@@ -419,19 +462,27 @@ _NO_WORKSPACE = _NoWorkspace()
 
 
 class DecodeStepGraph:
-    """pa_decode_append recorded once as a HIP graph (pa_decode_append_graph);
-    launch() replays it on the current (or given) stream.  The tensors are
-    kept alive by this object; refill their contents between launches."""
+    """pa_decode_append recorded once as a HIP graph (pa_decode_append_graph),
+    or pa_decode_append_fp8 (pa_decode_append_fp8_graph) when kv_scales =
+    (k_scale, v_scale) is given for fp8 caches; launch() replays it on the
+    current (or given) stream.  The tensors are kept alive by this object;
+    refill their contents between launches."""
 
     def __init__(self, out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
-                 workspace=None):
+                 workspace=None, kv_scales=None):
         lib = load_library()
-        args, ws = _decode_append_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale,
-                                       workspace, None)
-        self._keep = (out, q, key, value, k_cache, v_cache, block_tables, context_lens, ws)
         self._lib = lib
         self._h = ctypes.c_void_p()
-        _check(lib, "pa_decode_append_graph", lib.pa_decode_append_graph(ctypes.byref(self._h), *args[:-1]))
+        if kv_scales is None:
+            args, ws = _decode_append_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens,
+                                           scale, workspace, None)
+            _check(lib, "pa_decode_append_graph", lib.pa_decode_append_graph(ctypes.byref(self._h), *args[:-1]))
+        else:
+            args, ws = _decode_append_fp8_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens,
+                                               scale, kv_scales[0], kv_scales[1], workspace, None)
+            _check(lib, "pa_decode_append_fp8_graph",
+                   lib.pa_decode_append_fp8_graph(ctypes.byref(self._h), *args[:-1]))
+        self._keep = (out, q, key, value, k_cache, v_cache, block_tables, context_lens, ws)
         self._device = q.device
 
     def launch(self, stream=None) -> None:

@@ -308,3 +308,88 @@ def test_fp8_decode_in_a_pool_beyond_4gib_and_largest_group():
     torch.cuda.synchronize()
     ref = F.decode_fp8(q, kc, vc, bt, cl, scale, ks, vs)
     assert_attention_close(widen_dev(out), ref, "bf16", "fp8, pool > 4 GiB, group 64")
+
+
+def _fp8_step_case(name, num_seqs, seed, empty=()):
+    """A decode workload with its pool quantized by the oracle; sequences in
+    `empty` get context length 0 (nothing appended, zero output)."""
+    wl = W.make_workload(name, seed=seed, num_seqs=num_seqs)
+    cl = wl.context_lens.copy()
+    for s in empty:
+        cl[s] = 0
+    s_dec = wl.num_seqs
+    kn, vn = wl.k_new[-s_dec:], wl.v_new[-s_dec:]
+    slots = wl.slot_mapping[-s_dec:].copy()
+    slots[cl == 0] = -1
+    return wl, cl, kn, vn, slots, _quantize(wl.k_cache, K_SCALE), _quantize(wl.v_cache, V_SCALE)
+
+
+@pytest.mark.parametrize("name,num_seqs,seed,empty", [("llama3_8b", 16, 7, ()), ("qwen3_0p6b", 8, 8, (3,)),
+                                                      ("long_skewed", 2, 9, ()), ("llama3_8b", 128, 2, ())])
+def test_fp8_decode_append_matches_oracle(name, num_seqs, seed, empty):
+    """pa_decode_append_fp8: the caches bit for bit against the oracle's
+    quantized append of the step's new rows, the output against the fp64
+    oracle on the dequantized caches."""
+    wl, cl, kn, vn, slots, kc, vc = _fp8_step_case(name, num_seqs, seed, empty)
+    print(f"[gpu] fp8 step {name} S={num_seqs} seed={seed} empty={empty}", flush=True)
+    kc_d, vc_d = to_dev(kc), to_dev(vc)
+    out = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.decode_append_fp8(out, to_dev(wl.q), to_dev(kn), to_dev(vn), kc_d, vc_d, to_dev(wl.block_tables),
+                          to_dev(cl), wl.scale, K_SCALE, V_SCALE)
+    torch.cuda.synchronize()
+    F.reshape_and_cache_fp8(_as_f32(kn), _as_f32(vn), kc, vc, slots, K_SCALE, V_SCALE)
+    assert to_host(kc_d).tobytes() == kc.tobytes(), "fp8 step: K cache differs from the oracle"
+    assert to_host(vc_d).tobytes() == vc.tobytes(), "fp8 step: V cache differs from the oracle"
+    ref = F.decode_fp8(wl.q, kc, vc, wl.block_tables, cl, wl.scale, K_SCALE, V_SCALE)
+    got = widen_dev(out)
+    if empty:
+        assert np.all(got[list(empty)] == 0.0)
+    mx, rel = assert_attention_close(got, ref, "bf16", f"fp8 step {name}")
+    print(f"[gpu] fp8 step {name}: max-abs {mx:.3e} row-rel {rel:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name,num_seqs", [("llama3_8b", 16), ("long_skewed", 2)])
+def test_fp8_step_graph_replays_match_oracle(name, num_seqs):
+    """pa_decode_append_fp8_graph: every replay (inputs refilled from the
+    third on, caches restored, eager work in between) bit-exact in the caches
+    and within tolerance in the output; the eager call gives the same bits."""
+    wl, cl, kn0, vn0, slots, kc0, vc0 = _fp8_step_case(name, num_seqs, 61)
+    s = wl.num_seqs
+    kc, vc = to_dev(kc0), to_dev(vc0)
+    q, kn, vn = to_dev(wl.q), to_dev(kn0), to_dev(vn0)
+    bt, cld = to_dev(wl.block_tables), to_dev(cl)
+    out = torch.empty(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    g = ops.DecodeStepGraph(out, q, kn, vn, kc, vc, bt, cld, wl.scale, kv_scales=(K_SCALE, V_SCALE))
+    rng = np.random.default_rng(17)
+    scratch = torch.randn(1 << 20, device="cuda")
+    q_h, kn_h, vn_h = wl.q.copy(), kn0.copy(), vn0.copy()
+    for rep in range(4):
+        print(f"[gpu] fp8 graph {name} replay {rep}", flush=True)
+        if rep >= 2:
+            q_h = bf16_bits_from_float(rng.standard_normal(q_h.shape))
+            kn_h = bf16_bits_from_float(rng.standard_normal(kn_h.shape))
+            vn_h = bf16_bits_from_float(rng.standard_normal(vn_h.shape))
+            q.copy_(to_dev(q_h))
+            kn.copy_(to_dev(kn_h))
+            vn.copy_(to_dev(vn_h))
+        kc.copy_(to_dev(kc0))
+        vc.copy_(to_dev(vc0))
+        scratch.mul_(1.0001).add_(1.0)
+        torch.cuda.synchronize()
+        g.launch()
+        torch.cuda.synchronize()
+        got = to_host(out).copy()
+        okc, ovc = kc0.copy(), vc0.copy()
+        F.reshape_and_cache_fp8(_as_f32(kn_h), _as_f32(vn_h), okc, ovc, slots, K_SCALE, V_SCALE)
+        assert to_host(kc).tobytes() == okc.tobytes(), f"replay {rep}: fp8 K cache differs from the oracle"
+        assert to_host(vc).tobytes() == ovc.tobytes(), f"replay {rep}: fp8 V cache differs from the oracle"
+        ref = F.decode_fp8(q_h, okc, ovc, wl.block_tables, cl, wl.scale, K_SCALE, V_SCALE)
+        mx, rel = assert_attention_close(widen_dev(out), ref, "bf16", f"fp8 graph replay {rep}")
+        print(f"[gpu] fp8 graph {name} replay {rep}: max-abs {mx:.3e} row-rel {rel:.3e}", flush=True)
+        ekc, evc = to_dev(kc0), to_dev(vc0)
+        eout = torch.empty_like(out)
+        ops.decode_append_fp8(eout, q, kn, vn, ekc, evc, bt, cld, wl.scale, K_SCALE, V_SCALE)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(eout), got)
+        assert s == q_h.shape[0]
+    g.close()
