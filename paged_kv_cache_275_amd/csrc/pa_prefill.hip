@@ -59,7 +59,10 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_kernel(PrefillArgs
     // 45% fewer LDS bank-conflict cycles than D + 8 and 2.5% faster; D + 24,
     // D + 32 and D + 40 were no better than D + 8.
     constexpr int kKP = D + 16;
-    constexpr int kVP = kKT + 8;         // V^T row pitch in LDS (elements)
+    // V^T row pitch in LDS (elements).  kKT + 16 measured bank conflicts in
+    // 9% of the LDS-active cycles against 33% for kKT + 8 (the prefill time
+    // moved by less than 0.5%: the LDS is not what bounds it).
+    constexpr int kVP = kKT + 16;
     constexpr int kMs = D / 32;          // MFMA k-steps over dims
     constexpr int kDt = D / 16;          // 16-dim tiles of the output
     constexpr int kNT = NW * kWave;
