@@ -256,3 +256,42 @@ def test_stream_read_probe_argument_checks(lib):
     assert lib.pa_stream_read_probe(FAKE, 24, FAKE, None) == ops.PA_EINVAL
     assert lib.pa_stream_read_probe(ctypes.c_void_p(0x1008), 64, FAKE, None) == ops.PA_EINVAL
     assert lib.pa_stream_read_probe(None, 0, None, None) == ops.PA_OK
+
+
+def _decode_append_fp8(lib, graph=False, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=4, cl=FAKE, s=2, hq=8, hkv=2,
+             d=128, bs=16, nb=64, scale=0.1, ks=0.02, vs=0.03, dtype=ops.PA_BF16, ws=FAKE, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    args = (a["out"], a["q"], a["key"], a["value"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["s"], a["hq"],
+            a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["ks"], a["vs"], a["dtype"], a["ws"], a["ws_bytes"])
+    if graph:
+        h = ctypes.c_void_p()
+        rc = lib.pa_decode_append_fp8_graph(ctypes.byref(h), *args)
+        assert not h.value, "a rejected call must not return a graph"
+        return rc
+    return lib.pa_decode_append_fp8(*args, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(key=None), ops.PA_EINVAL),                   # the step needs the new rows
+    (dict(value=None), ops.PA_EINVAL),
+    (dict(dtype=ops.PA_F32), ops.PA_EUNSUPPORTED),     # fp8 caches go with bf16 q/out/rows
+    (dict(s=0, ks=0.0), ops.PA_EINVAL),
+    (dict(s=0, vs=float("nan")), ops.PA_EINVAL),
+    (dict(d=96), ops.PA_EUNSUPPORTED),
+    (dict(hq=6, hkv=4), ops.PA_EINVAL),
+    (dict(ws_bytes=16), ops.PA_EWORKSPACE),
+    (dict(s=8193), ops.PA_EUNSUPPORTED),
+])
+def test_decode_append_fp8_rejects(lib, kw, code):
+    """Rejected before anything is enqueued (FAKE pointers are never touched)."""
+    assert _decode_append_fp8(lib, **kw) == code
+    assert _decode_append_fp8(lib, graph=True, **kw) == code
+
+
+def test_decode_append_fp8_graph_needs_sequences(lib):
+    assert _decode_append_fp8(lib, graph=True, s=0) == ops.PA_EINVAL
+    assert lib.pa_decode_append_fp8_graph(None, *([FAKE] * 7), 4, FAKE, 2, 8, 2, 128, 16, 64, 0.1, 0.02,
+                                          0.03, ops.PA_BF16, FAKE, 1 << 30) == ops.PA_EINVAL
+    assert _decode_append_fp8(lib, s=0, q=None, out=None) == ops.PA_OK   # empty batch: nothing to do
