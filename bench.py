@@ -275,11 +275,13 @@ def fp8_prefill(wl, pools, pre, stream):
             "fp8_prefill_note": f"pa_prefill_chunk_fp8 on the workload's chunks over an fp8 pool copy, mean of {reps}"}
 
 
-def fp8_decode(wl, pools, q, bt, cl, ws, stream):
+def fp8_decode(wl, pools, q, kn, vn, bt, cl, ws, stream):
     """Decode over fp8 E4M3 copies of the pools (pa_decode_fp8), outside the
     timed region.  The copies are quantized on the GPU by
     pa_reshape_and_cache_fp8 over every slot of each pool; decode reads one
-    byte per K/V element, so its KV bytes are half the bf16 step's."""
+    byte per K/V element, so its KV bytes are half the bf16 step's.  Also the
+    whole fp8 decode step, pa_decode_append_fp8 (quantized append of the new
+    rows, then decode), back to back over the same copies."""
     import numpy as np
     import torch
 
@@ -295,7 +297,8 @@ def fp8_decode(wl, pools, q, bt, cl, ws, stream):
         k8 = torch.empty(kc.shape, dtype=torch.uint8, device=q.device)
         v8 = torch.empty(vc.shape, dtype=torch.uint8, device=q.device)
         ops.reshape_and_cache_fp8(kc.view(-1, hkv, d), vc.view(-1, hkv, d), k8, v8, slots, ks, vs)
-        calls.append((ops.bind_decode_fp8(out8, q, k8, v8, bt, cl, wl.scale, ks, vs, workspace=ws), k8, v8))
+        calls.append((ops.bind_decode_fp8(out8, q, k8, v8, bt, cl, wl.scale, ks, vs, workspace=ws), k8, v8,
+                      ops.bind_decode_append_fp8(out8, q, kn, vn, k8, v8, bt, cl, wl.scale, ks, vs, workspace=ws)))
     for i in range(8):
         calls[i % len(calls)][0]()
     reps = 40
@@ -314,6 +317,15 @@ def fp8_decode(wl, pools, q, bt, cl, ws, stream):
     torch.cuda.synchronize()
     k_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
     call_us = call_ev[0].elapsed_time(call_ev[1]) * 1e3 / reps
+    for i in range(8):
+        calls[i % len(calls)][3]()
+    torch.cuda.synchronize()
+    call_ev[0].record(stream)
+    for i in range(reps):
+        calls[i % len(calls)][3]()
+    call_ev[1].record(stream)
+    torch.cuda.synchronize()
+    step_us = call_ev[0].elapsed_time(call_ev[1]) * 1e3 / reps
     fp8_bytes = wl.decode_kv_bytes() // wl.elem_bytes      # one byte per element
     gbs = fp8_bytes / (k_us * 1e-6) / 1e9
     return {"fp8_decode_stream_kernel_us": round(k_us, 2),
@@ -321,8 +333,11 @@ def fp8_decode(wl, pools, q, bt, cl, ws, stream):
             "fp8_decode_kv_bytes": fp8_bytes,
             "fp8_decode_kernel_gbs": round(gbs, 1),
             "fp8_decode_kernel_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "fp8_step_us": round(step_us, 2),
+            "fp8_step_kv_gbs": round(fp8_bytes / (step_us * 1e-6) / 1e9, 1),
             "fp8_decode_note": f"pa_decode_fp8 over {len(calls)} fp8 pool copies, mean of {reps} back-to-back calls; "
-                               "kernel time from HIP events set at its dispatch"}
+                               "kernel time from HIP events set at its dispatch; fp8_step_us: pa_decode_append_fp8 "
+                               "(quantized append + decode), mean of the same number of back-to-back calls"}
 
 
 def prefill_flops(wl) -> int:
@@ -763,7 +778,7 @@ def main():
     if not args.unfused:
         res["extras"].update(graph_step(wl, pools, pre, out, q, k_new[t_new - s_dec:], v_new[t_new - s_dec:], bt, cl,
                                         ws, stream))
-    res["extras"].update(fp8_decode(wl, pools, q, bt, cl, ws, stream))
+    res["extras"].update(fp8_decode(wl, pools, q, k_new[t_new - s_dec:], v_new[t_new - s_dec:], bt, cl, ws, stream))
     res["extras"].update(fp8_prefill(wl, pools, pre, stream))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
