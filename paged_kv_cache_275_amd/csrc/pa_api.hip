@@ -279,10 +279,7 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.n_kvg = num_kv_heads * a.groups_per_kv;
     // wave groups of n_kvg waves (one per head group), as many as fit the
     // persistent grid and the workspace records
-    const bool two_groups_fit = (head_dim == 64 || gp <= 4) &&
-                                2 * pa::decode_lds_bytes(head_dim, gp, num_seqs) <= pa::kLdsBytesPerCU;
-    const int per_cu = kv8 && two_groups_fit ? pa::kDecodeWavesPerCUFp8 : pa::kDecodeWavesPerCU;
-    a.wave_groups = std::max(1, std::min(decode_waves(per_cu), pa::kDecodeMaxWaves) / a.n_kvg);
+    a.wave_groups = std::max(1, std::min(decode_waves(pa::kDecodeWavesPerCU), pa::kDecodeMaxWaves) / a.n_kvg);
     if ((long long)a.wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
     a.waves = a.wave_groups * a.n_kvg;
     // a caller's workspace is laid out for every launch shape; the fixed
@@ -330,9 +327,7 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.scale_log2 = (kv8 ? scale * kv8->k : scale) * 1.4426950408889634f;
     a.v_scale = kv8 ? kv8->v : 1.0f;
     const int ov_stages = g_override_stages.load(std::memory_order_relaxed);
-    const int stages = ov_stages > 0 ? ov_stages
-                                     : (per_cu == pa::kDecodeWavesPerCUFp8 ? pa::kDecodeStagesFp8Pair
-                                                                           : pa::kDecodeStages);
+    const int stages = ov_stages > 0 ? ov_stages : pa::kDecodeStages;
     hipError_t e = pa::launch_decode(a, dtype == PA_BF16, head_dim, gp, stages, kv8 != nullptr,
                                      static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(kernel_start), static_cast<hipEvent_t>(kernel_stop));

@@ -24,11 +24,13 @@
 //  * Each wave owns ALL query heads (up to GP) that share the kv head, so every
 //    K/V byte is read from HBM exactly once and reused from registers by the
 //    whole GQA group.
-//  * Lane layout for one block: lane = 8*tg + dl.  Token group tg (0..7) owns
-//    tokens tg and tg+8.  Each load instruction makes the 8 lanes of a token
-//    group read one contiguous 128-byte line of the token's row (16 bytes per
-//    lane); chunk c of lane dl holds dims c*8*E + dl*E .. +E (E = elements per
-//    16 bytes), so every fetched line is consumed by a single instruction.
+//  * Lane layout for one block, bf16 queries: lane = 16*q + r.  For the
+//    scores lane r loads 16 bytes of token r's key row per MFMA step; for
+//    P*V lane (q, r) loads D/16 contiguous dims (r*D/16 ..) of tokens 4q ..
+//    4q+3, so each load instruction reads four whole 128-byte (fp8) or
+//    256-byte (bf16) head rows.  fp32 path: lane = 8*tg + dl, token group tg
+//    (0..7) owns tokens tg and tg+8, and chunk c of lane dl holds dims
+//    c*8*E + dl*E .. +E (E = elements per 16 bytes).
 //  * K/V are loaded with the non-temporal hint (read once, never reused).
 //  * A ring of STAGES blocks is in flight per wave: the loads of unit x+STAGES
 //    are issued as soon as unit x has been consumed (unconditionally, so that
@@ -37,19 +39,22 @@
 //    staged per wave in LDS up front, so no load waits on a block-table read.
 //    The query rows of a segment are loaded once, during the segment's first
 //    unit for the wave's first segment and during the previous segment's last
-//    unit otherwise, into registers (MFMA A operands); loading them with
+//    unit otherwise, into registers (MFMA B operands); loading them with
 //    every unit instead measured 4.7 us slower on llama3_8b (50% more load
 //    instructions, all L2 hits).
-//  * Scores: bf16 on the matrix cores (Q, GP heads padded to 16 rows, times
-//    K^T of the block's 16 tokens); fp32 by FMA dot products summed over the 8
-//    lanes of a token group by three DPP adds.  Online softmax in the log2
-//    domain with a wave-uniform running max per head that is only raised when
-//    a block holds a score more than kRescaleSlack above it (ballot -> uniform
-//    branch): the same softmax, with rare accumulator rescales and
-//    exp2 <= 2^kRescaleSlack.
-//  * P*V: probabilities packed to bf16 pairs (token tg, token tg+8); V
-//    re-paired by v_perm so one v_dot2 adds both tokens.  The normaliser is
-//    summed from the same rounded probabilities.
+//  * bf16 queries: scores and P*V on the matrix cores.  The scores come out
+//    transposed (S^T = K Q^T, 16x16x32 steps: the block's 16 tokens by 16 score
+//    columns, head g of the group in column g*16/GP), so each lane ends with
+//    one column's scores for four tokens: after the softmax these are the A
+//    operand of O = P V (16x16x16 steps, one per dim of the lane's D/16), with
+//    no exchange between lanes.  The output row of head g then lies whole in
+//    the lanes of one 16-lane row.  fp32: FMA dot products summed over the 8
+//    lanes of a token group by DPP, and P*V by FMA.
+//  * Online softmax in the log2 domain with a running max per head that is
+//    only raised when a block holds a score more than kRescaleSlack above it
+//    (ballot -> uniform branch): the same softmax, with rare accumulator
+//    rescales and exp2 <= 2^kRescaleSlack.  Probabilities enter P*V rounded
+//    to bf16, and the normaliser sums the same rounded values.
 //  * A segment that one wave covers entirely is normalised and written to out.
 //    A segment split across waves leaves (max, sum, unnormalised acc) records
 //    in the workspace (slot 0: the wave's first segment, slot 1: its last) and
@@ -72,7 +77,7 @@
 //    reads that token's K/V rows from the inputs; the merge kernel copies them
 //    into the cache afterwards.
 //  * FP8 E4M3 caches (KV8 instances): the same kernel on byte caches, the bytes
-//    converted exactly to bf16 operands; see decode_stream_kernel.
+//    converted exactly to bf16 MFMA operands; see decode_stream_kernel.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -98,12 +103,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Finished segments are staged in LDS and written out once the wave's loads are
 // done (see the kernel).  A slot holds one segment: a header of 4 words, two
-// floats per head, and the wave's reduced sums (GP*D floats).  Slots per wave:
+// floats per head, and the wave's sums (GP*D floats; with fewer than 4 heads
+// the matrix-core layout leaves lanes without a head, so 4*D).  Slots per wave:
 // about 8 KB of LDS, at least 2.
 template <int GP, int D>
 struct StageGeom {
     static constexpr int kMeta = 4 + 2 * GP;
-    static constexpr int kVals = GP * D;
+    static constexpr int kVals = (GP < 4 ? 4 : GP) * D;
     static constexpr int kWords = kMeta + kVals;
     static constexpr int kSlots = (2048 / kVals) > 2 ? (2048 / kVals) : 2;
     static constexpr size_t kBytesPerWave = (size_t)kSlots * kWords * sizeof(float);
@@ -121,129 +127,84 @@ struct DecodeGeom {
     __device__ static constexpr int dim(int c, int dl, int j) { return c * 8 * kE + dl * kE + j; }
 };
 
-// Scores of the lane's two tokens for its GP heads, fully reduced over dims.
-template <typename T, int GP, int KDPL, int KVECS, int KQB>
-__device__ __forceinline__ void qk_block(float (&sc)[2][GP], const uint4 (&kr)[2][KVECS],
-                                         const uint32_t (&qb)[GP][KQB], const float (&qf)[GP][KDPL]) {
+// fp32: scores of the lane's two tokens for its GP heads, fully reduced over dims.
+template <int GP, int KDPL, int KVECS>
+__device__ __forceinline__ void qk_block(float (&sc)[2][GP], const uint4 (&kr)[2][KVECS], const float (&qf)[GP][KDPL]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
             float a = 0.f;
-            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                for (int c = 0; c < KVECS; ++c) {
-                    a = dot2_bf16(kr[t][c].x, qb[g][c * 4 + 0], a);
-                    a = dot2_bf16(kr[t][c].y, qb[g][c * 4 + 1], a);
-                    a = dot2_bf16(kr[t][c].z, qb[g][c * 4 + 2], a);
-                    a = dot2_bf16(kr[t][c].w, qb[g][c * 4 + 3], a);
-                }
-            } else {
-#pragma unroll
-                for (int c = 0; c < KVECS; ++c) {
-                    a = fmaf(__uint_as_float(kr[t][c].x), qf[g][c * 4 + 0], a);
-                    a = fmaf(__uint_as_float(kr[t][c].y), qf[g][c * 4 + 1], a);
-                    a = fmaf(__uint_as_float(kr[t][c].z), qf[g][c * 4 + 2], a);
-                    a = fmaf(__uint_as_float(kr[t][c].w), qf[g][c * 4 + 3], a);
-                }
+            for (int c = 0; c < KVECS; ++c) {
+                a = fmaf(__uint_as_float(kr[t][c].x), qf[g][c * 4 + 0], a);
+                a = fmaf(__uint_as_float(kr[t][c].y), qf[g][c * 4 + 1], a);
+                a = fmaf(__uint_as_float(kr[t][c].z), qf[g][c * 4 + 2], a);
+                a = fmaf(__uint_as_float(kr[t][c].w), qf[g][c * 4 + 3], a);
             }
             sc[t][g] = sum_lanes8(a);
         }
     }
 }
 
-// bf16: acc[g][:] += p0 * V[token 0] + p1 * V[token 1], with (p0, p1) of head g
-// given as a packed bf16 pair pk[g]; l[g] += p0 + p1 as rounded.
-template <int GP, int KDPL, int KVECS>
-__device__ __forceinline__ void pv_block_packed(float (&acc)[GP][KDPL], float (&l)[GP], const uint32_t (&pk)[GP],
-                                                const uint4 (&vr)[2][KVECS]) {
+// O += P V for one block on the matrix cores (16x16x16 bf16 steps).  Lane
+// (q, r) = (lane/16, lane%16) holds, as the A operand, the probabilities of
+// score column r for tokens 4q .. 4q+3 (two bf16 pairs: pk), and vw[k], the KW
+// words of its KNT = D/16 contiguous dims r*KNT .. of token 4q+k.  Step j
+// takes dim j of every lane's dims as B column r, so o[j] receives output rows
+// 4q .. 4q+3 (score columns) at dim r*KNT + j.  B needs the four tokens of one
+// dim in one lane; v_perm pairs tokens (4q, 4q+1) and (4q+2, 4q+3) of a dim
+// (bf16: word w holds dims 2w, 2w+1; fp8: dims 4w .. 4w+3, converted exactly).
+template <int KNT, int KW, bool KV8>
+__device__ __forceinline__ void pv_mfma(f32x4_t (&o)[KNT], uint2 pk, const uint32_t (&vw)[4][KW]) {
+    if constexpr (!KV8) {
+        static_assert(KNT == 2 * KW, "bf16: two dims per word");
 #pragma unroll
-    for (int g = 0; g < GP; ++g) l[g] = dot2_bf16(pk[g], 0x3F803F80u, l[g]);
-#pragma unroll
-    for (int c = 0; c < KVECS; ++c) {
-        const uint32_t v0[4] = {vr[0][c].x, vr[0][c].y, vr[0][c].z, vr[0][c].w};
-        const uint32_t v1[4] = {vr[1][c].x, vr[1][c].y, vr[1][c].z, vr[1][c].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // (even dim of token 0, even dim of token 1) and the odd dims
-            const uint32_t ev = __builtin_amdgcn_perm(v1[j], v0[j], 0x05040100u);
-            const uint32_t od = __builtin_amdgcn_perm(v1[j], v0[j], 0x07060302u);
-#pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                acc[g][c * 8 + 2 * j] = dot2_bf16(ev, pk[g], acc[g][c * 8 + 2 * j]);
-                acc[g][c * 8 + 2 * j + 1] = dot2_bf16(od, pk[g], acc[g][c * 8 + 2 * j + 1]);
-            }
-        }
-    }
-}
-
-// FP8 E4M3 V: as pv_block_packed, from the raw bytes of the lane's KDPL
-// contiguous dims of tokens 0 and 1 (vr[t][0]; KDPL = 8 uses .x and .y).  The
-// bytes of the two tokens are interleaved by v_perm and converted in pairs
-// (exactly) to the bf16 pairs v_dot2 takes.
-template <int GP, int KDPL>
-__device__ __forceinline__ void pv_block_fp8(float (&acc)[GP][KDPL], float (&l)[GP], const uint32_t (&pk)[GP],
-                                             const uint4 (&vr)[2][1]) {
-#pragma unroll
-    for (int g = 0; g < GP; ++g) l[g] = dot2_bf16(pk[g], 0x3F803F80u, l[g]);
-    const uint32_t v0[4] = {vr[0][0].x, vr[0][0].y, vr[0][0].z, vr[0][0].w};
-    const uint32_t v1[4] = {vr[1][0].x, vr[1][0].y, vr[1][0].z, vr[1][0].w};
-#pragma unroll
-    for (int w = 0; w < KDPL / 4; ++w) {
-        // (t0 d, t1 d, t0 d+1, t1 d+1) and the same for d+2, d+3
-        const uint32_t lo = __builtin_amdgcn_perm(v1[w], v0[w], 0x05010400u);
-        const uint32_t hi = __builtin_amdgcn_perm(v1[w], v0[w], 0x07030602u);
-        const uint32_t pr[4] = {fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
-                                fp8x2_to_bf16x2<true>(hi)};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int g = 0; g < GP; ++g) acc[g][4 * w + i] = dot2_bf16(pr[i], pk[g], acc[g][4 * w + i]);
-        }
-    }
-}
-
-// acc[g][:] += p[0][g] * V[token 0] + p[1][g] * V[token 1]   (the lane's dims)
-template <typename T, int GP, int KDPL, int KVECS>
-__device__ __forceinline__ void pv_block(float (&acc)[GP][KDPL], float (&l)[GP], const float (&p)[2][GP],
-                                         const uint4 (&vr)[2][KVECS]) {
-    if constexpr (sizeof(T) == 2) {
-        uint32_t pk[GP];
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            pk[g] = pack_bf16x2(p[0][g], p[1][g]);
-            l[g] = dot2_bf16(pk[g], 0x3F803F80u, l[g]);  // + p0 + p1 as rounded
-        }
-#pragma unroll
-        for (int c = 0; c < KVECS; ++c) {
-            const uint32_t v0[4] = {vr[0][c].x, vr[0][c].y, vr[0][c].z, vr[0][c].w};
-            const uint32_t v1[4] = {vr[1][c].x, vr[1][c].y, vr[1][c].z, vr[1][c].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // (even dim of token 0, even dim of token 1) and the odd dims
-                const uint32_t ev = __builtin_amdgcn_perm(v1[j], v0[j], 0x05040100u);
-                const uint32_t od = __builtin_amdgcn_perm(v1[j], v0[j], 0x07060302u);
-#pragma unroll
-                for (int g = 0; g < GP; ++g) {
-                    acc[g][c * 8 + 2 * j] = dot2_bf16(ev, pk[g], acc[g][c * 8 + 2 * j]);
-                    acc[g][c * 8 + 2 * j + 1] = dot2_bf16(od, pk[g], acc[g][c * 8 + 2 * j + 1]);
-                }
-            }
+        for (int w = 0; w < KW; ++w) {
+            const uint2 ev = make_uint2(__builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x05040100u),
+                                        __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x05040100u));
+            const uint2 od = make_uint2(__builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x07060302u),
+                                        __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x07060302u));
+            o[2 * w] = mfma16x16x16_bf16(pk, ev, o[2 * w]);
+            o[2 * w + 1] = mfma16x16x16_bf16(pk, od, o[2 * w + 1]);
         }
     } else {
+        static_assert(KNT == 4 * KW, "fp8: four dims per word");
 #pragma unroll
-        for (int g = 0; g < GP; ++g) l[g] += p[0][g] + p[1][g];
+        for (int w = 0; w < KW; ++w) {
+            // (token a dim d, token b dim d, token a dim d+1, token b dim d+1)
+            const uint32_t lo0 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x05010400u);
+            const uint32_t hi0 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x07030602u);
+            const uint32_t lo1 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x05010400u);
+            const uint32_t hi1 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x07030602u);
+            o[4 * w + 0] = mfma16x16x16_bf16(
+                pk, make_uint2(fp8x2_to_bf16x2<false>(lo0), fp8x2_to_bf16x2<false>(lo1)), o[4 * w + 0]);
+            o[4 * w + 1] = mfma16x16x16_bf16(
+                pk, make_uint2(fp8x2_to_bf16x2<true>(lo0), fp8x2_to_bf16x2<true>(lo1)), o[4 * w + 1]);
+            o[4 * w + 2] = mfma16x16x16_bf16(
+                pk, make_uint2(fp8x2_to_bf16x2<false>(hi0), fp8x2_to_bf16x2<false>(hi1)), o[4 * w + 2]);
+            o[4 * w + 3] = mfma16x16x16_bf16(
+                pk, make_uint2(fp8x2_to_bf16x2<true>(hi0), fp8x2_to_bf16x2<true>(hi1)), o[4 * w + 3]);
+        }
+    }
+}
+
+// fp32: acc[g][:] += p[0][g] * V[token 0] + p[1][g] * V[token 1]   (the lane's dims)
+template <int GP, int KDPL, int KVECS>
+__device__ __forceinline__ void pv_block(float (&acc)[GP][KDPL], float (&l)[GP], const float (&p)[2][GP],
+                                         const uint4 (&vr)[2][KVECS]) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+    for (int g = 0; g < GP; ++g) l[g] += p[0][g] + p[1][g];
 #pragma unroll
-            for (int c = 0; c < KVECS; ++c) {
-                const float v[4] = {__uint_as_float(vr[t][c].x), __uint_as_float(vr[t][c].y),
-                                    __uint_as_float(vr[t][c].z), __uint_as_float(vr[t][c].w)};
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+        for (int c = 0; c < KVECS; ++c) {
+            const float v[4] = {__uint_as_float(vr[t][c].x), __uint_as_float(vr[t][c].y),
+                                __uint_as_float(vr[t][c].z), __uint_as_float(vr[t][c].w)};
 #pragma unroll
-                    for (int g = 0; g < GP; ++g) acc[g][c * 4 + j] = fmaf(p[t][g], v[j], acc[g][c * 4 + j]);
-                }
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int g = 0; g < GP; ++g) acc[g][c * 4 + j] = fmaf(p[t][g], v[j], acc[g][c * 4 + j]);
             }
         }
     }
@@ -251,12 +212,9 @@ __device__ __forceinline__ void pv_block(float (&acc)[GP][KDPL], float (&l)[GP],
 
 // A register copy the compiler cannot fold away: the result never shares a
 // register with its source, so the source registers are free once it has run.
-__device__ __forceinline__ uint4 opaque_copy(uint4 x) {
-    uint4 y;
-    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.x) : "v"(x.x));
-    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.y) : "v"(x.y));
-    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.z) : "v"(x.z));
-    asm volatile("v_mov_b32 %0, %1" : "=&v"(y.w) : "v"(x.w));
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t x) {
+    uint32_t y;
+    asm volatile("v_mov_b32 %0, %1" : "=&v"(y) : "v"(x));
     return y;
 }
 
@@ -456,19 +414,19 @@ __device__ __forceinline__ int block_at_tick(long long t, long long T, const int
 
 // KV8: the caches hold FP8 E4M3 (q and out stay T = bf16); dequantized values
 // are k_scale * e4m3 and v_scale * e4m3, k_scale folded into scale_log2 and
-// v_scale applied when a segment closes.  A lane then holds kDpl CONTIGUOUS
-// dims of V (one chunk of kE = kDpl bytes), and for scores lane group g loads
-// the 16 bytes at dims 64p + 16g of a key, which feed MFMA steps 2p and 2p+1
-// (the query rows are loaded with the same dim order).
+// v_scale applied when a segment closes.  For the scores lane row q loads the
+// 16 bytes at dims 64p + 16q of a key, which feed MFMA steps 2p and 2p+1 (the
+// query rows are loaded with the same dim order); V bytes are converted in
+// pv_mfma.
 template <typename T, int D, int GP, int NW, int STAGES, int WIN, bool KV8>
 __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a) {
     using G = DecodeGeom<T, D>;
     using KVT = typename std::conditional<KV8, uint8_t, T>::type;  // cache element
     static_assert(!KV8 || sizeof(T) == 2, "an fp8 cache goes with bf16 queries");
     constexpr int kDpl = G::kDpl;
-    constexpr int kVecs = KV8 ? 1 : G::kVecs;
+    constexpr int kVecs = G::kVecs;
     constexpr int kQb = G::kQb;
-    constexpr int kE = KV8 ? kDpl : G::kE;
+    constexpr int kE = G::kE;
 
     extern __shared__ int smem[];
     __shared__ int2 scan_scratch[NW];
@@ -543,15 +501,36 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     int seg_first_blk = cblk;
     bool first_seg = true;
 
-    // bf16: scores come from MFMA.  Lane l holds token l%16 of the block as
-    // MFMA column and the heads 4*(l/16) .. +3 as MFMA rows.
+    // bf16 queries: both products on the matrix cores.  Lane (mrow, mtok) =
+    // (l/16, l%16).  Scores come out transposed, S^T = K Q^T: K is the A
+    // operand (row mtok = token mtok of the block), the query rows the B
+    // operand, so lane l receives the scores of score column mtok for tokens
+    // 4*mrow .. +3 -- exactly the A operand of P*V (pv_mfma) once turned into
+    // probabilities, with no exchange between lanes.  Head g of the group sits
+    // in score column g*kCs; the other columns carry no head (their
+    // probabilities are zero).  P*V row c is score column c, so head g's
+    // output lands in rows g*kCs: on lanes with mrow = g*kCs/4, accumulator
+    // element g*kCs%4, dims mtok*kNt .. +kNt of the head (every lane holds a
+    // whole head at 4 heads or more).
     constexpr bool kMfma = sizeof(T) == 2;
-    constexpr int kMf = D / 32;        // MFMAs per block
-    constexpr int kRows = (GP + 3) / 4;  // 16-lane row groups that hold heads
+    constexpr int kMf = D / 32;         // score MFMAs per block
+    constexpr int kNt = D / 16;         // P*V MFMAs per block = dims per lane
+    constexpr int kVw = kNt * (int)sizeof(KVT) / 4;  // dwords of V per lane and token
+    constexpr int kCs = 16 / GP;        // score columns per head
+    constexpr int kU = GP > 4 ? GP / 4 : 1;  // accumulator elements holding a head
     const int mrow = lane >> 4;
     const int mtok = lane & 15;
     const uint32_t kmf_off = ((uint32_t)mtok * hkv_heads) * D + (KV8 ? 16 : 8) * mrow;
-    uint32_t* lp = reinterpret_cast<uint32_t*>(tabs + NW * WIN) + (wv % NW) * (4 * 8 * 4);
+    // this lane's score column holds head mtok / kCs
+    const bool real_col = mtok % kCs == 0 && mtok / kCs < nvh;
+    // V: tokens 4*mrow + k (k = 0..3), dims mtok*kNt .. +kNt
+    const uint32_t vmf_off = ((uint32_t)(4 * mrow) * hkv_heads) * D + (uint32_t)mtok * kNt;
+    const uint32_t tok_off = (uint32_t)hkv_heads * D;
+    // head of accumulator element u*kCs of this lane (rows 4*mrow + u*kCs), or -1
+    auto out_head = [&](int u) -> int {
+        const int row = 4 * mrow + (GP > 4 ? u * kCs : 0);
+        return row % kCs == 0 && row / kCs < nvh ? row / kCs : -1;
+    };
 
     // Staging of finished segments.  A global store holds up the completion
     // count of every load issued after it until the store itself completes,
@@ -559,9 +538,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     // mid-stream stalls the ring.  So finished segments wait in LDS and are
     // written after the wave's last load (or when the slots run out).
     using SG = StageGeom<GP, D>;
-    constexpr int kCh = GP * kDpl / 8;  // reduced sums per lane
-    float* stage = reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(tabs + NW * WIN) + NW * (4 * 8 * 4)) +
-                   (wv % NW) * SG::kSlots * SG::kWords;
+    constexpr int kCh = kMfma ? kU * kNt : GP * kDpl / 8;  // staged sums per lane
+    float* stage = reinterpret_cast<float*>(tabs + NW * WIN) + (wv % NW) * SG::kSlots * SG::kWords;
     int nstaged = 0;
     const int gl = (tg * kCh) / kDpl;  // head of this lane's reduced sums
     const int d0 = (tg * kCh) % kDpl;  // their first element among the lane's dims
@@ -582,13 +560,31 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             float v[kCh];
 #pragma unroll
             for (int i = 0; i < kCh; ++i) v[i] = sl[SG::kMeta + i * kWave + lane];
-            const float x = sl[4 + gl], y = sl[4 + GP + gl];
-            if (gl < nvh) {
-                if (kind == 0) {
-                    store_run<T, kE, kCh>(reinterpret_cast<T*>(a.out) + (size_t)(base + gl) * D, v, x, d0, dl);
-                } else {
-                    store_run<float, kE, kCh>(a.ws_acc + (size_t)(base + gl) * D, v, 1.f, d0, dl);
-                    if (dl == 0 && d0 == 0) *reinterpret_cast<float2*>(a.ws_ml + (size_t)(base + gl) * 2) = make_float2(x, y);
+            if constexpr (kMfma) {
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int h = out_head(u);
+                    if (h < 0) continue;
+                    const float x = sl[4 + h], y = sl[4 + GP + h];
+                    if (kind == 0) {
+                        store_piece<T, kNt>(reinterpret_cast<T*>(a.out) + (size_t)(base + h) * D + mtok * kNt,
+                                            &v[u * kNt], x);
+                    } else {
+                        float* dst = a.ws_acc + (size_t)(base + h) * D + mtok * kNt;
+#pragma unroll
+                        for (int i = 0; i < kNt; i += 4) store_piece<float, 4>(dst + i, &v[u * kNt + i], 1.f);
+                        if (mtok == 0) *reinterpret_cast<float2*>(a.ws_ml + (size_t)(base + h) * 2) = make_float2(x, y);
+                    }
+                }
+            } else {
+                const float x = sl[4 + gl], y = sl[4 + GP + gl];
+                if (gl < nvh) {
+                    if (kind == 0) {
+                        store_run<T, kE, kCh>(reinterpret_cast<T*>(a.out) + (size_t)(base + gl) * D, v, x, d0, dl);
+                    } else {
+                        store_run<float, kE, kCh>(a.ws_acc + (size_t)(base + gl) * D, v, 1.f, d0, dl);
+                        if (dl == 0 && d0 == 0) *reinterpret_cast<float2*>(a.ws_ml + (size_t)(base + gl) * 2) = make_float2(x, y);
+                    }
                 }
             }
         }
@@ -604,12 +600,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 
     uint32_t qb[GP][kQb], qnb[GP][kQb];
     float qf[GP][kDpl], qnf[GP][kDpl];
-    // MFMA path: the A operands (query rows of the head group, padded to 16
-    // rows) of the current segment, and of the next one, loaded during the last
-    // unit of the current segment
+    // MFMA path: the B operands of the scores (the group's query rows in
+    // their score columns; columns without a head repeat the first head's row,
+    // never used) of the current segment, and of the next one, loaded during
+    // the last unit of the current segment
     uint4 qm[kMf], qmn[kMf];
     auto load_qm = [&](uint4 (&dst)[kMf], int seq) __attribute__((always_inline)) {
-        const uint32_t hi = mtok < nvh ? (uint32_t)mtok : 0u;
+        const uint32_t hi = real_col ? (uint32_t)(mtok / kCs) : 0u;
         const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)seq * a.num_q_heads + h0 + hi) * D;
 #pragma unroll
         for (int mm = 0; mm < kMf; ++mm) {
@@ -624,7 +621,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     }
 
     float m[GP], l[GP], acc[GP][kDpl];
-    float mlane[4];  // MFMA layout: running max of the heads of this lane's rows
+    // MFMA path: running max and partial normaliser of this lane's score
+    // column (the max is the same on the column's four lanes; the normaliser
+    // covers the lane's tokens), and the P*V accumulators
+    float mcol = -INFINITY, lcol = 0.f;
+    f32x4_t oacc[kNt];
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
         m[g] = -INFINITY;
@@ -633,10 +634,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         for (int i = 0; i < kDpl; ++i) acc[g][i] = 0.f;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
+    for (int j = 0; j < kNt; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     uint4 kr[STAGES][2][kVecs], vr[STAGES][2][kVecs];
     uint4 kb4[STAGES][kMf];
+    uint32_t vt[STAGES][4][kVw];  // MFMA path: V of tokens 4*mrow + k
     int vld[STAGES];
 
     auto issue = [&](int st, uint4 e) {
@@ -644,28 +646,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         const uint32_t hv = __builtin_amdgcn_readfirstlane(e.y);
         vld[st] = (int)(hv >> 16);
         const size_t base = ((size_t)b * kBlockTokens * hkv_heads + (hv & 0xFFFFu)) * D;
-        // rows of the block's two token halves (V, and K on the fp32 path); with
-        // a fused append, the block holding a sequence's new token (e.w = its
-        // input row) reads that token's rows from the inputs: the lane choice
-        // changes addresses only, never the number of loads
+        // with a fused append, the block holding a sequence's new token (e.w =
+        // its input row) reads that token's rows from the inputs: the lane
+        // choice changes addresses only, never the number of loads
         const uint32_t nrow = __builtin_amdgcn_readfirstlane(e.w);
         const int noff = vld[st] - 1;  // the new token is the block's last valid one
-        const KVT* vb0 = vbase + base + lane_off;
-        const KVT* vb1 = vb0 + tok8_off;
-        const KVT* kt0 = kbase + base + lane_off;
-        const KVT* kt1 = kt0 + tok8_off;
-        if (!KV8 && nrow != 0xFFFFFFFFu) {
-            const size_t in_off = (size_t)nrow * D + dl * kE;
-            if (tg == noff) {
-                vb0 = reinterpret_cast<const KVT*>(a.new_v) + in_off;
-                kt0 = reinterpret_cast<const KVT*>(a.new_k) + in_off;
-            }
-            if (tg + 8 == noff) {
-                vb1 = reinterpret_cast<const KVT*>(a.new_v) + in_off;
-                kt1 = reinterpret_cast<const KVT*>(a.new_k) + in_off;
-            }
-        }
         if constexpr (kMfma) {
+            // K: token mtok, 16 bytes per score step; V: tokens 4*mrow + k
             const KVT* kb = kbase + base + kmf_off;
             if (!KV8 && nrow != 0xFFFFFFFFu && mtok == noff)
                 kb = reinterpret_cast<const KVT*>(a.new_k) + (size_t)nrow * D + 8 * mrow;
@@ -676,48 +663,97 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 #pragma unroll
                 for (int mm = 0; mm < kMf; ++mm) kb4[st][mm] = ldg_nt(kb + 32 * mm);
             }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const KVT* vp = vbase + base + vmf_off + k * tok_off;
+                if (!KV8 && nrow != 0xFFFFFFFFu && 4 * mrow + k == noff)
+                    vp = reinterpret_cast<const KVT*>(a.new_v) + (size_t)nrow * D + mtok * kNt;
+                ldg_nt_words<kVw>(vt[st][k], vp);
+            }
         } else {
+            // K and V rows of the block's two token halves (tokens tg, tg + 8)
+            const KVT* vb0 = vbase + base + lane_off;
+            const KVT* vb1 = vb0 + tok8_off;
+            const KVT* kt0 = kbase + base + lane_off;
+            const KVT* kt1 = kt0 + tok8_off;
+            if (nrow != 0xFFFFFFFFu) {
+                const size_t in_off = (size_t)nrow * D + dl * kE;
+                if (tg == noff) {
+                    vb0 = reinterpret_cast<const KVT*>(a.new_v) + in_off;
+                    kt0 = reinterpret_cast<const KVT*>(a.new_k) + in_off;
+                }
+                if (tg + 8 == noff) {
+                    vb1 = reinterpret_cast<const KVT*>(a.new_v) + in_off;
+                    kt1 = reinterpret_cast<const KVT*>(a.new_k) + in_off;
+                }
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int c = 0; c < kVecs; ++c)
-                    kr[st][t][c] = ldg_nt((t == 0 ? kt0 : kt1) + c * 8 * kE);
+                for (int c = 0; c < kVecs; ++c) kr[st][t][c] = ldg_nt((t == 0 ? kt0 : kt1) + c * 8 * kE);
             }
-        }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if constexpr (KV8 && kDpl == 8) {  // 8 bytes per lane and token
-                const uint2 v = *reinterpret_cast<const uint2*>(t == 0 ? vb0 : vb1);
-                vr[st][t][0] = make_uint4(v.x, v.y, 0u, 0u);
-            } else {
+            for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int c = 0; c < kVecs; ++c)
-                    vr[st][t][c] = ldg_nt((t == 0 ? vb0 : vb1) + c * 8 * kE);
+                for (int c = 0; c < kVecs; ++c) vr[st][t][c] = ldg_nt((t == 0 ? vb0 : vb1) + c * 8 * kE);
             }
         }
     };
 
-    // Segment (cs, kvg) is done: stage its rows, or a partial record.  The
-    // partial sums are reduce-scattered over the token groups, so lane (tg, dl)
-    // ends with kCh complete sums of head gl: elements d0 .. d0+kCh-1 of its dims.
+    // Segment (cs, kvg) is done: stage its rows, or a partial record.  MFMA
+    // path: each lane holds whole sums (kNt dims of each of its kU heads).
+    // fp32: the partial sums are reduce-scattered over the token groups, so
+    // lane (tg, dl) ends with kCh complete sums of head gl: elements d0 ..
+    // d0+kCh-1 of its dims.
     auto finish_segment = [&]() {
         const bool complete = seg_first_blk == 0 && cblk == cnb - 1;
         const int slot = first_seg ? 0 : 1;
         float red[kCh];
-        reduce_scatter8<GP, kDpl>(red, acc, lane);
-        if constexpr (KV8) {
-#pragma unroll
-            for (int i = 0; i < kCh; ++i) red[i] *= a.v_scale;  // dequantized V = v_scale * e4m3
-        }
         float* sl = stage + nstaged * SG::kWords;
+        if constexpr (kMfma) {
+            // the rows of this lane's heads, whole: no reduction across lanes
 #pragma unroll
-        for (int i = 0; i < kCh; ++i) sl[SG::kMeta + i * kWave + lane] = red[i];
+            for (int u = 0; u < kU; ++u) {
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            const float lt = sum_groups8(l[g]);  // the same on every lane
-            if (lane == 0) {
-                sl[4 + g] = complete ? 1.f / lt : m[g];
-                sl[4 + GP + g] = lt;
+                for (int j = 0; j < kNt; ++j) red[u * kNt + j] = oacc[j][GP > 4 ? u * kCs : 0];
+            }
+            if constexpr (KV8) {
+#pragma unroll
+                for (int i = 0; i < kCh; ++i) red[i] *= a.v_scale;  // dequantized V = v_scale * e4m3
+            }
+#pragma unroll
+            for (int i = 0; i < kCh; ++i) sl[SG::kMeta + i * kWave + lane] = red[i];
+            const float lt = sum_rows4(lcol);  // column total, on the column's four lanes
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                const float lg = readlane_f32(lt, g * kCs), mg = readlane_f32(mcol, g * kCs);
+                if (lane == 0) {
+                    sl[4 + g] = complete ? 1.f / lg : mg;
+                    sl[4 + GP + g] = lg;
+                }
+            }
+            mcol = -INFINITY;
+            lcol = 0.f;
+#pragma unroll
+            for (int j = 0; j < kNt; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+            reduce_scatter8<GP, kDpl>(red, acc, lane);
+#pragma unroll
+            for (int i = 0; i < kCh; ++i) sl[SG::kMeta + i * kWave + lane] = red[i];
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                const float lt = sum_groups8(l[g]);  // the same on every lane
+                if (lane == 0) {
+                    sl[4 + g] = complete ? 1.f / lt : m[g];
+                    sl[4 + GP + g] = lt;
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                m[g] = -INFINITY;
+                l[g] = 0.f;
+#pragma unroll
+                for (int d = 0; d < kDpl; ++d) acc[g][d] = 0.f;
             }
         }
         if (lane == 0) {
@@ -725,15 +761,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             sl[1] = __int_as_float(complete ? cs * a.num_q_heads + h0 : (wv * 2 + slot) * GP);
         }
         ++nstaged;
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            m[g] = -INFINITY;
-            l[g] = 0.f;
-#pragma unroll
-            for (int d = 0; d < kDpl; ++d) acc[g][d] = 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mlane[r] = -INFINITY;
         if (!complete && seg_first_blk == 0) {
             // this wave holds the segment's first unit: note it for the fix-up,
             // with the wave (same head group) whose group holds the first tick
@@ -796,27 +823,27 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 
                 const int valid = vld[st];
                 if constexpr (kMfma) {
-                    // ---- scores: S[head][token] = Q K^T on the matrix cores
+                    // ---- scores on the matrix cores, transposed: S^T = K Q^T
                     f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
                     if constexpr (KV8) {
 #pragma unroll
                         for (int p = 0; p < kMf / 2; ++p) {
                             const uint4 r = kb4[st][p];
-                            s4 = mfma16x16x32_bf16(qm[2 * p], fp8x8_to_bf16x8(r.x, r.y), s4);
-                            s4 = mfma16x16x32_bf16(qm[2 * p + 1], fp8x8_to_bf16x8(r.z, r.w), s4);
+                            s4 = mfma16x16x32_bf16(fp8x8_to_bf16x8(r.x, r.y), qm[2 * p], s4);
+                            s4 = mfma16x16x32_bf16(fp8x8_to_bf16x8(r.z, r.w), qm[2 * p + 1], s4);
                         }
                     } else {
 #pragma unroll
-                        for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(qm[mm], kb4[st][mm], s4);
+                        for (int mm = 0; mm < kMf; ++mm) s4 = mfma16x16x32_bf16(kb4[st][mm], qm[mm], s4);
                     }
                     // V leaves the ring for working registers, and the stage is
                     // refilled at once: the loads of unit ux + STAGES then run
                     // during this unit's softmax and P*V instead of after them.
-                    uint4 vw[2][kVecs];
+                    uint32_t vw[4][kVw];
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int k = 0; k < 4; ++k) {
 #pragma unroll
-                        for (int c = 0; c < kVecs; ++c) vw[t][c] = opaque_copy(vr[st][t][c]);
+                        for (int w = 0; w < kVw; ++w) vw[k][w] = opaque_copy(vt[st][k][w]);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(s4[r]));
@@ -826,70 +853,49 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                     if (valid < kBlockTokens) {
                         // stale slots past the context: zero their V (may hold NaN)
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            if (tg + 8 * t >= valid) {
+                        for (int k = 0; k < 4; ++k) {
+                            if (4 * mrow + k >= valid) {
 #pragma unroll
-                                for (int c = 0; c < kVecs; ++c) vw[t][c] = make_uint4(0, 0, 0, 0);
+                                for (int w = 0; w < kVw; ++w) vw[k][w] = 0u;
                             }
                         }
                     }
+                    // this lane's scores: column mtok, tokens 4*mrow + i
                     float sv[4];
                     bool need = false;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        sv[r] = mtok < valid ? s4[r] * a.scale_log2 : -INFINITY;
-                        need |= (4 * mrow + r < GP) && sv[r] > mlane[r] + kRescaleSlack;
+                    for (int i = 0; i < 4; ++i) {
+                        sv[i] = 4 * mrow + i < valid ? s4[i] * a.scale_log2 : -INFINITY;
+                        need |= real_col && sv[i] > mcol + kRescaleSlack;
                     }
                     // ---- lazy running max (rare, uniform branch)
                     if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                        float bm4[4];
+                        const float bm = max_rows4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+                        const float mn = fmaxf(mcol, bm);
+                        // 0 when the column's max was -inf; columns without a head keep 1
+                        const float alpha = real_col ? fast_exp2(mcol - mn) : 1.f;
+                        mcol = mn;
+                        lcol *= alpha;
+                        // accumulator element i of this lane is output row
+                        // 4*mrow + i, i.e. score column 4*mrow + i: its factor
+                        // comes from lane 16*mrow + 4*mrow + i
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) bm4[r] = max_row16(sv[r]);
+                        for (int u = 0; u < kU; ++u) {
+                            const int i = GP > 4 ? u * kCs : 0;
+                            const float ar = __int_as_float(
+                                __builtin_amdgcn_ds_bpermute((20 * mrow + i) * 4, __float_as_int(alpha)));
 #pragma unroll
-                        for (int g = 0; g < GP; ++g) {
-                            const float bm = readlane_f32(bm4[g % 4], 16 * (g / 4));
-                            const float mn = fmaxf(m[g], bm);
-                            const float alpha = fast_exp2(m[g] - mn);  // 0 when m was -inf
-                            l[g] *= alpha;
-#pragma unroll
-                            for (int d = 0; d < kDpl; ++d) acc[g][d] *= alpha;
-                            m[g] = mn;
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float v = m[r < GP ? r : 0];
-#pragma unroll
-                            for (int rg = 1; rg < kRows; ++rg) {
-                                if (4 * rg + r < GP && mrow == rg) v = m[4 * rg + r];
-                            }
-                            mlane[r] = v;
+                            for (int jt = 0; jt < kNt; ++jt) oacc[jt][i] *= ar;
                         }
                     }
-                    // ---- probabilities, paired (token t, token t+8), to the P*V layout
-                    uint32_t pk4[4];
+                    // ---- probabilities of the lane's four tokens: the A operand of P*V
+                    float pr[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float pr = fast_exp2(sv[r] - mlane[r]);
-                        pk4[r] = pack_bf16x2(pr, dpp_f32<kDppRowRor8>(pr));
-                    }
-                    if (mtok < 8 && mrow < kRows) {
-                        *reinterpret_cast<uint4*>(lp + (mrow * 8 + mtok) * 4) = make_uint4(pk4[0], pk4[1], pk4[2], pk4[3]);
-                    }
-                    uint32_t pk[GP];
-#pragma unroll
-                    for (int rg = 0; rg < kRows; ++rg) {
-                        const uint4 v = *reinterpret_cast<const uint4*>(lp + (rg * 8 + tg) * 4);
-                        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            if (4 * rg + r < GP) pk[4 * rg + r] = vv[r];
-                        }
-                    }
-                    if constexpr (KV8) {
-                        pv_block_fp8<GP, kDpl>(acc, l, pk, vw);
-                    } else {
-                        pv_block_packed<GP, kDpl, kVecs>(acc, l, pk, vw);
-                    }
+                    for (int i = 0; i < 4; ++i) pr[i] = real_col ? fast_exp2(sv[i] - mcol) : 0.f;
+                    const uint2 pk = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+                    lcol = dot2_bf16(pk.x, 0x3F803F80u, lcol);  // + the rounded probabilities
+                    lcol = dot2_bf16(pk.y, 0x3F803F80u, lcol);
+                    pv_mfma<kNt, kVw, KV8>(oacc, pk, vw);
                 } else {
                     if (valid < kBlockTokens) {
                         // stale slots past the context: zero their V (may hold NaN)
@@ -903,7 +909,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                     }
                     // ---- scores of this block
                     float sc[2][GP];
-                    qk_block<T, GP, kDpl, kVecs, kQb>(sc, kr[st], qb, qf);
+                    qk_block<GP, kDpl, kVecs>(sc, kr[st], qf);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -931,7 +937,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 #pragma unroll
                         for (int g = 0; g < GP; ++g) p[t][g] = fast_exp2(sc[t][g] - m[g]);
                     }
-                    pv_block<T, GP, kDpl, kVecs>(acc, l, p, vr[st]);
+                    pv_block<GP, kDpl, kVecs>(acc, l, p, vr[st]);
                     // ---- refill this stage (unconditionally, see above), once
                     // its registers are no longer read
                     keep_in_regs<GP, kDpl>(acc, l);
@@ -1100,7 +1106,6 @@ template <int GP, int D>
 static size_t decode_stream_lds_bytes(int num_seqs) {
     return 2 * (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int) +
            (size_t)kDecodeWaves * kDecodeWindow * sizeof(uint4) +
-           (size_t)kDecodeWaves * 4 * 8 * 4 * sizeof(uint32_t) +
            (size_t)kDecodeWaves * StageGeom<GP, D>::kBytesPerWave;
 }
 
@@ -1157,23 +1162,6 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int stages, bool 
         case 2: return launch_decode_g<T, D, 2>(a, stages, kv8, stream, e0, e1);
         case 4: return launch_decode_g<T, D, 4>(a, stages, kv8, stream, e0, e1);
         default: return launch_decode_g<T, D, 8>(a, stages, kv8, stream, e0, e1);
-    }
-}
-
-size_t decode_lds_bytes(int head_dim, int gp, int num_seqs) {
-    if (head_dim == 64) {
-        switch (gp) {
-            case 1: return decode_stream_lds_bytes<1, 64>(num_seqs);
-            case 2: return decode_stream_lds_bytes<2, 64>(num_seqs);
-            case 4: return decode_stream_lds_bytes<4, 64>(num_seqs);
-            default: return decode_stream_lds_bytes<8, 64>(num_seqs);
-        }
-    }
-    switch (gp) {
-        case 1: return decode_stream_lds_bytes<1, 128>(num_seqs);
-        case 2: return decode_stream_lds_bytes<2, 128>(num_seqs);
-        case 4: return decode_stream_lds_bytes<4, 128>(num_seqs);
-        default: return decode_stream_lds_bytes<8, 128>(num_seqs);
     }
 }
 

@@ -106,6 +106,41 @@ __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(uint4 a, uint4 b, f32x4_t c
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// D[16x16] += A[16x16] * B[16x16] in bf16 with fp32 accumulation.  Lane l holds
+// A row l%16 and B column l%16, k-slots 4*(l/16) .. +4 (4 bf16 in two dwords,
+// slot 0 in the low half of the first); it receives D column l%16, rows
+// 4*(l/16) .. +3.
+__device__ __forceinline__ f32x4_t mfma16x16x16_bf16(uint2 a, uint2 b, f32x4_t c) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                     0, 0, 0);
+}
+
+// Sum and max over the four 16-lane rows (lanes l, l^16, l^32, l^48) by the
+// gfx950 permlane swaps; every lane gets the result.
+__device__ __forceinline__ float sum_rows4(float x) {
+    {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+__device__ __forceinline__ float max_rows4(float x) {
+    {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return x;
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -133,6 +168,22 @@ __device__ __forceinline__ uint4 ldg_nt(const void* p) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// KW consecutive dwords (KW = 1, 2 or 4, aligned to their size), non-temporal.
+template <int KW>
+__device__ __forceinline__ void ldg_nt_words(uint32_t (&dst)[KW], const void* p) {
+    if constexpr (KW == 4) {
+        const uint4 v = ldg_nt(p);
+        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    } else if constexpr (KW == 2) {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        dst[0] = v.x; dst[1] = v.y;
+    } else {
+        static_assert(KW == 1, "1, 2 or 4 dwords");
+        dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
 }
 
 // ---- FP8 E4M3 (OCP "E4M3FN": bias 7, largest finite 448, no infinities).

@@ -11,19 +11,16 @@ namespace pa {
 // block) units with kDecodeStages blocks in flight; block ids are staged in
 // LDS kDecodeWindow units at a time.
 constexpr int kDecodeWaves = 4;
-// Default ring depth: 2 blocks per wave measured best (llama3_8b 91.8 vs
-// 92.7 us at 4, qwen3_0p6b 33.5 vs 34.6 us); 3 and 4 are also built (fp8
-// caches: 2, 3, 4, 6, 8).
+// Default ring depth: 2 blocks per wave measured best, for bf16 and fp8
+// caches alike (llama3_8b: 81.0 us bf16 and 46.4 us fp8 at 2, 46.7 / 47.2 /
+// 48.1 us fp8 at 3 / 4 / 6); 3 and 4 are also built (fp8 caches: 2, 3, 4, 6,
+// 8).
 constexpr int kDecodeStages = 2;
 constexpr int kDecodeWindow = 256;
+// One wave per SIMD.  fp8 caches too: their units have half the bytes of a
+// bf16 unit and the same matrix-core work, and a second wave per SIMD (8 per
+// compute unit) measured slower (llama3_8b 48.6 against 46.4 us).
 constexpr int kDecodeWavesPerCU = 4;
-// An fp8 cache halves the bytes per unit but not the instructions: with two
-// waves per SIMD one wave's arithmetic covers the other's waits.  Used when
-// two workgroups fit a compute unit (registers: head_dim 64 or at most 4 heads
-// per wave; LDS: see decode_lds_bytes).
-constexpr int kDecodeWavesPerCUFp8 = 8;
-constexpr int kDecodeStagesFp8Pair = 2;  // blocks in flight per wave when two waves share a SIMD
-constexpr size_t kLdsBytesPerCU = 160 * 1024;
 constexpr int kDecodeMaxWaves = 4096;   // workspace records are sized for this many waves
 constexpr int kDecodeMaxSeqs = 8192;    // sequence prefix sums live in LDS
 // Work-split costs: closing a segment takes about as long as streaming one
@@ -101,8 +98,6 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int total_rows, in
 // Launches the streaming kernel and the split-segment merge.  Non-null events
 // receive the streaming kernel's start and stop times.  kv8: the caches hold
 // FP8 E4M3 (bf16 queries only; 2, 3, 4, 6 or 8 stages).
-// LDS bytes one workgroup of the streaming kernel uses for num_seqs sequences.
-size_t decode_lds_bytes(int head_dim, int gp, int num_seqs);
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int head_dim, int gp, int stages, bool kv8,
                          hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
