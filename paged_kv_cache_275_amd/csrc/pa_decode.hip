@@ -314,23 +314,44 @@ __device__ __forceinline__ void store_run(OutT* dst, const float (&v)[CH], float
 // running max).  pref[s] = blocks of sequences before s and tpref[s] = ticks of
 // one head group of every sequence before s, computed by all NT threads of the
 // workgroup: per-thread sums over a chunk of sequences, a scan within each
-// wave, and one barrier to add the totals of the waves before.
+// wave, and one barrier to add the totals of the waves before.  Each context
+// length is read from memory once (a thread's loads are all issued before the
+// first use) and kept in lens[] for the rest of the kernel; reading it again
+// after the barrier would add a dependent round trip to every wave's prologue.
+// The first four loads are issued unconditionally (clamped addresses), so the
+// wait for each is exact.
 template <int NT>
-__device__ void prefix_blocks(int* pref, int* tpref, int2* wave_tot, const int32_t* __restrict__ ctx, int S,
-                              int unit_ticks, int switch_ticks) {
+__device__ void prefix_blocks(int* pref, int* tpref, int* lens, int2* wave_tot, const int32_t* __restrict__ ctx,
+                              int S, int unit_ticks, int switch_ticks) {
     constexpr int NW = NT / kWave;
     const int t = threadIdx.x;
     const int w = t / kWave;
     const int chunk = (S + NT - 1) / NT;
     const int lo = min(S, t * chunk);
     const int hi = min(S, lo + chunk);
-    auto nblk = [&](int s) { return (ctx[s] + kBlockTokens - 1) / kBlockTokens; };
+    auto nblk = [&](int n) { return (n + kBlockTokens - 1) / kBlockTokens; };
     auto ticks = [&](int nb) { return nb * unit_ticks + (nb > 0 ? switch_ticks : 0); };
     int sx = 0, sy = 0;
-    for (int s = lo; s < hi; ++s) {
-        const int nb = nblk(s);
+    auto take = [&](int s, int n) {
+        lens[s] = n;
+        const int nb = nblk(n);
         sx += nb;
         sy += ticks(nb);
+    };
+    int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = ctx[min(lo + j, S - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (lo + j < hi) take(lo + j, c[j]);
+    }
+    for (int s0 = lo + 4; s0 < hi; s0 += 4) {  // more than 4*NT sequences
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = ctx[min(s0 + j, S - 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (s0 + j < hi) take(s0 + j, c[j]);
+        }
     }
     const int ix = wave_scan_incl(sx), iy = wave_scan_incl(sy);
     if ((t & (kWave - 1)) == kWave - 1) wave_tot[w] = make_int2(ix, iy);
@@ -347,7 +368,7 @@ __device__ void prefix_blocks(int* pref, int* tpref, int2* wave_tot, const int32
     for (int s = lo; s < hi; ++s) {
         pref[s] = rx;
         tpref[s] = ry;
-        const int nb = nblk(s);
+        const int nb = nblk(lens[s]);
         rx += nb;
         ry += ticks(nb);
     }
@@ -357,13 +378,29 @@ __device__ void prefix_blocks(int* pref, int* tpref, int2* wave_tot, const int32
     }
 }
 
-// Largest s in [0, S) with n_kvg * pref[s] <= u (u < n_kvg * pref[S]); that
-// sequence has at least one block.
-__device__ __forceinline__ int find_seq(const int* pref, int S, int n_kvg, long long u) {
-    int lo = 0, hi = S - 1;
+// Largest s in [lo, hi) with key[s] <= t, for key nondecreasing on [lo, hi)
+// and key[lo] <= t.  Wave-uniform: all 64 lanes take part (each step tests
+// 64 evenly spaced candidates and keeps the last that passes), so the search
+// over S keys costs ceil(log64 S) LDS round trips instead of log2 S.
+__device__ __forceinline__ int wave_search(const int* key, int lo, int hi, long long t) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int n = hi - lo;
+    while (n > 1) {
+        const int step = (n + kWave - 1) / kWave;
+        const bool ok = lane * step < n && (long long)key[lo + lane * step] <= t;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(ok);  // lanes 0 .. k pass, lane 0 always
+        const int k = 63 - __builtin_clzll(m);
+        lo += k * step;
+        n = min(step, n - k * step);
+    }
+    return lo;
+}
+
+// Per-lane form: largest s in [lo, hi] with key[s] <= t (key[lo] <= t).
+__device__ __forceinline__ int lane_search(const int* key, int lo, int hi, long long t) {
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((long long)n_kvg * pref[mid] <= u) lo = mid; else hi = mid - 1;
+        if ((long long)key[mid] <= t) lo = mid; else hi = mid - 1;
     }
     return lo;
 }
@@ -406,7 +443,7 @@ __device__ __forceinline__ long long range_start(long long g, long long T, long 
 __device__ __forceinline__ int block_at_tick(long long t, long long T, const int* pref, const int* tpref, int S,
                                              int R) {
     if (t >= T) return pref[S];
-    const int s = find_seq(tpref, S, 1, t);
+    const int s = wave_search(tpref, 0, S, t);
     const int nb = pref[s + 1] - pref[s];
     const int r = (int)(t - tpref[s]);
     return pref[s] + min((r + R - 1) / R, nb);
@@ -431,13 +468,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     extern __shared__ int smem[];
     __shared__ int2 scan_scratch[NW];
     const int S = a.num_seqs;
+    const int S4 = (S + 1 + 3) & ~3;
     int* pref = smem;
-    int* tpref = smem + ((S + 1 + 3) & ~3);
-    uint4* tabs = reinterpret_cast<uint4*>(smem + 2 * ((S + 1 + 3) & ~3));
+    int* tpref = smem + S4;
+    int* lens = smem + 2 * S4;  // context lengths
+    uint4* tabs = reinterpret_cast<uint4*>(smem + 3 * S4);
 
     const int R = a.unit_ticks;
     const int C = a.switch_ticks;
-    prefix_blocks<NW * kWave>(pref, tpref, scan_scratch, a.context_lens, S, R, C);
+    prefix_blocks<NW * kWave>(pref, tpref, lens, scan_scratch, a.context_lens, S, R, C);
     __syncthreads();
     const int n_kvg = a.n_kvg;
     const long long TT = tpref[S];  // ticks of one head group over all sequences
@@ -495,7 +534,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     const KVT* vbase = reinterpret_cast<const KVT*>(a.v_cache);
 
     // consume-side position: sequence, block, blocks in sequence
-    int cs = find_seq(pref, S, 1, u_begin);
+    int cs = wave_search(pref, 0, S, u_begin);
     int cnb = pref[cs + 1] - pref[cs];
     int cblk = u_begin - pref[cs];
     int seg_first_blk = cblk;
@@ -777,12 +816,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     for (int wb0 = u_begin; wb0 < u_end; wb0 += WIN) {
         const int wn = min(WIN, u_end - wb0);
         // ---- stage this window's block ids and valid-token counts in LDS
+        // (the window's units lie in sequences s_a .. s_b)
+        const int s_a = wb0 == u_begin ? cs : wave_search(pref, 0, S, wb0);
+        const int s_b = wave_search(pref, s_a, S, wb0 + wn - 1);
         for (int i = lane; i < wn; i += kWave) {
             const int u = wb0 + i;
-            const int s = find_seq(pref, S, 1, u);
+            const int s = lane_search(pref, s_a, s_b, u);
             const int blk = u - pref[s];
             const int b = a.block_tables[(size_t)s * a.max_blocks_per_seq + blk];
-            const int valid = min(kBlockTokens, a.context_lens[s] - blk * kBlockTokens);
+            const int valid = min(kBlockTokens, lens[s] - blk * kBlockTokens);
             // block id; kv head | valid tokens << 16; (unused); input row of
             // the new token if this block holds it (fused append), else ~0
             const bool holds_new = a.new_k != nullptr && blk == pref[s + 1] - pref[s] - 1;
@@ -1104,7 +1146,7 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
 // ---------------------------------------------------------------- launchers
 template <int GP, int D>
 static size_t decode_stream_lds_bytes(int num_seqs) {
-    return 2 * (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int) +
+    return 3 * (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int) +
            (size_t)kDecodeWaves * kDecodeWindow * sizeof(uint4) +
            (size_t)kDecodeWaves * StageGeom<GP, D>::kBytesPerWave;
 }
