@@ -121,7 +121,6 @@ struct DecodeGeom {
     static constexpr int kE = 16 / kElem;            // elements per 16-byte chunk
     static constexpr int kDpl = D / 8;               // dims per lane
     static constexpr int kVecs = kDpl / kE;          // 16-byte chunks per lane per token
-    static constexpr int kQb = kDpl / 2 > 0 ? kDpl / 2 : 1;
     static_assert(kVecs >= 1, "head_dim too small");
     // global dim of element j of chunk c of lane dl
     __device__ static constexpr int dim(int c, int dl, int j) { return c * 8 * kE + dl * kE + j; }
@@ -405,14 +404,13 @@ __device__ __forceinline__ int lane_search(const int* key, int lo, int hi, long 
     return lo;
 }
 
-// Query rows of the GP heads of head group kvg of sequence s, this lane's dims.
-template <typename T, int D, int GP, int KDPL, int KQB>
-__device__ __forceinline__ void load_q(uint32_t (&qb)[GP][KQB], float (&qf)[GP][KDPL], const DecodeArgs& a,
-                                       int s, int kvg, int dl) {
-    using G = DecodeGeom<T, D>;
+// fp32: query rows of the GP heads of head group kvg of sequence s, this lane's dims.
+template <int D, int GP, int KDPL>
+__device__ __forceinline__ void load_q(float (&qf)[GP][KDPL], const DecodeArgs& a, int s, int kvg, int dl) {
+    using G = DecodeGeom<float, D>;
     const int hk = kvg / a.groups_per_kv;
     const int gi0 = (kvg % a.groups_per_kv) * GP;
-    const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)s * a.num_q_heads + hk * a.group + gi0) * D;
+    const float* qrow = reinterpret_cast<const float*>(a.q) + ((size_t)s * a.num_q_heads + hk * a.group + gi0) * D;
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
         // heads past the group (GP > group) reuse the first head's row: their
@@ -421,14 +419,9 @@ __device__ __forceinline__ void load_q(uint32_t (&qb)[GP][KQB], float (&qf)[GP][
         const int gl = gi0 + g < a.group ? g : 0;
 #pragma unroll
         for (int c = 0; c < G::kVecs; ++c) {
-            const uint4 v = *reinterpret_cast<const uint4*>(qrow + (size_t)gl * D + G::dim(c, dl, 0));
-            if constexpr (sizeof(T) == 2) {
-                qb[g][c * 4 + 0] = v.x; qb[g][c * 4 + 1] = v.y;
-                qb[g][c * 4 + 2] = v.z; qb[g][c * 4 + 3] = v.w;
-            } else {
-                qf[g][c * 4 + 0] = __uint_as_float(v.x); qf[g][c * 4 + 1] = __uint_as_float(v.y);
-                qf[g][c * 4 + 2] = __uint_as_float(v.z); qf[g][c * 4 + 3] = __uint_as_float(v.w);
-            }
+            const float4 v = *reinterpret_cast<const float4*>(qrow + (size_t)gl * D + G::dim(c, dl, 0));
+            qf[g][c * 4 + 0] = v.x; qf[g][c * 4 + 1] = v.y;
+            qf[g][c * 4 + 2] = v.z; qf[g][c * 4 + 3] = v.w;
         }
     }
 }
@@ -462,7 +455,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     static_assert(!KV8 || sizeof(T) == 2, "an fp8 cache goes with bf16 queries");
     constexpr int kDpl = G::kDpl;
     constexpr int kVecs = G::kVecs;
-    constexpr int kQb = G::kQb;
     constexpr int kE = G::kE;
 
     extern __shared__ int smem[];
@@ -637,7 +629,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
         __builtin_amdgcn_s_waitcnt(0);
     };
 
-    uint32_t qb[GP][kQb], qnb[GP][kQb];
     float qf[GP][kDpl], qnf[GP][kDpl];
     // MFMA path: the B operands of the scores (the group's query rows in
     // their score columns; columns without a head repeat the first head's row,
@@ -656,7 +647,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     if constexpr (kMfma) {
         load_qm(qm, cs);
     } else {
-        load_q<T, D, GP, kDpl, kQb>(qb, qf, a, cs, kvg, dl);
+        load_q<D, GP, kDpl>(qf, a, cs, kvg, dl);
     }
 
     float m[GP], l[GP], acc[GP][kDpl];
@@ -859,7 +850,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                     if constexpr (kMfma) {
                         load_qm(qmn, ns);
                     } else {
-                        load_q<T, D, GP, kDpl, kQb>(qnb, qnf, a, ns, kvg, dl);
+                        load_q<D, GP, kDpl>(qnf, a, ns, kvg, dl);
                     }
                 }
 
@@ -1004,8 +995,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
                     } else {
 #pragma unroll
                         for (int g = 0; g < GP; ++g) {
-#pragma unroll
-                            for (int i = 0; i < kQb; ++i) qb[g][i] = qnb[g][i];
 #pragma unroll
                             for (int i = 0; i < kDpl; ++i) qf[g][i] = qnf[g][i];
                         }

@@ -22,9 +22,6 @@ constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
 constexpr int kDppRowRor8 = 0x128;     // lane i <- lane (i+8) mod 16 within a row
-constexpr int kDppRowRor4 = 0x124;
-constexpr int kDppRowRor2 = 0x122;
-constexpr int kDppRowRor1 = 0x121;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -67,22 +64,10 @@ __device__ __forceinline__ float sum_groups8(float x) {
     return x;
 }
 
-// Max over the 16 lanes of each row (every lane of the row gets it).
-__device__ __forceinline__ float max_row16(float x) {
-    x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
-    x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
-    x = fmaxf(x, dpp_f32<kDppRowRor2>(x));
-    x = fmaxf(x, dpp_f32<kDppRowRor1>(x));
-    return x;
-}
-
 __device__ __forceinline__ float readlane_f32(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-// D[16x16] += A[16x32] * B[32x16] in bf16 with fp32 accumulation.  Lane l holds
-// A row l%16 and B column l%16, k-slots 8*(l/16) .. +8 (8 bf16 in 16 bytes);
-// it receives D column l%16, rows 4*(l/16) .. +3.
 // Inclusive prefix sum over the 64 lanes of a wave: row_shr 1, 2, 4, 8 within
 // each 16-lane row, then row 0's total into row 1 and row 2's into row 3
 // (row_bcast:15), then the first two rows' total into rows 2 and 3
@@ -101,6 +86,9 @@ __device__ __forceinline__ int wave_scan_incl(int x) {
     return x;
 }
 
+// D[16x16] += A[16x32] * B[32x16] in bf16 with fp32 accumulation.  Lane l holds
+// A row l%16 and B column l%16, k-slots 8*(l/16) .. +8 (8 bf16 in 16 bytes);
+// it receives D column l%16, rows 4*(l/16) .. +3.
 __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
