@@ -1030,11 +1030,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 // costs two dependent round trips.  In the fused call the workgroup first
 // copies new K/V rows into the cache (see below).  Records of zero weight (m = -inf: waves
 // whose range was empty) are skipped without touching their sums.
+//
+// Workgroup b merges for wave w = (b mod 8) * waves/8 + b/8: workgroups are
+// dealt to the XCDs round robin (b mod 8), and the streaming kernel placed
+// waves [x*waves/8, (x+1)*waves/8) on XCD x, so the note and most records are
+// read on the XCD that wrote them (measured on MI355X: 0.4-0.8 us off a
+// decode step).  The row copies stay dealt by b, spread over all XCDs.
 template <typename T, int D, int GP>
 __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) {
     constexpr int kPerLane = D / kWave;  // 1 or 2
     constexpr int kBatch = 8;
-    const int w = blockIdx.x;
+    const int nb = (int)gridDim.x;  // = a.waves
+    const int w = nb % 8 == 0 ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
     const SplitNote sn = a.ws_split[w];
@@ -1062,7 +1069,7 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
     if (merging) load_batch(0);  // in flight while the copy below resolves its slot
 
     if (a.new_k != nullptr) {
-        // Fused KV append: the new token's K/V rows of sequence w (and w +
+        // Fused KV append: the new token's K/V rows of sequence b (and b +
         // gridDim.x, ...) go to their cache slots (position N-1).  The streaming
         // kernel took those rows from the inputs, so the copies only have to be
         // done by the end of the call.  The rows and the context length load
@@ -1073,7 +1080,7 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
         const int row_vecs = a.num_kv_heads * kRowVecsPerHead;
         const int bd = (int)blockDim.x;
         const int chunk = 4 * bd;  // one chunk at the configurations' shapes
-        for (int sq = w; sq < a.num_seqs; sq += gridDim.x) {
+        for (int sq = (int)blockIdx.x; sq < a.num_seqs; sq += gridDim.x) {
             const uint4* ksrc = reinterpret_cast<const uint4*>(a.new_k) + (size_t)sq * row_vecs;
             const uint4* vsrc = reinterpret_cast<const uint4*>(a.new_v) + (size_t)sq * row_vecs;
             for (int c0 = 0; c0 < row_vecs; c0 += chunk) {
