@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <mutex>
 
@@ -106,6 +107,29 @@ int decode_waves(int per_cu) {
     w = (w / pa::kDecodeWaves) * pa::kDecodeWaves;
     if (w < pa::kDecodeWaves) w = pa::kDecodeWaves;
     return (int)w;
+}
+
+// Bands of the decode grid (see DecodeArgs).  With a bf16 cache, head_dim 128,
+// 8 kv heads and one head group per kv head -- 2 KB token rows -- the waves
+// of kv heads 4..7 stream measurably slower than those of heads 0..3 (3.5% per
+// block on MI355X, whichever compute units they run on: the second half of
+// every token row is slower to read).  Those heads then get their own band
+// with kDecodeBandRatio times the wave groups of the first half, so that both
+// halves finish together.  Otherwise (including fp8 caches, 1 KB rows, where
+// the split measured slower) one band of n_kvg head groups.
+void decode_bands(pa::DecodeArgs& a, int wave_groups, int num_kv_heads, bool bf16_rows_2k) {
+    if (bf16_rows_2k && num_kv_heads == 8 && a.groups_per_kv == 1 && wave_groups >= 2) {
+        const int total = 2 * wave_groups;  // groups of 4 waves
+        int g0 = (int)std::lround(total / (1.0 + pa::kDecodeBandRatio));
+        g0 = std::max(1, std::min(total - 1, g0));
+        a.band_heads = 4;
+        a.band_groups[0] = g0;
+        a.band_groups[1] = total - g0;
+    } else {
+        a.band_heads = a.n_kvg;
+        a.band_groups[0] = wave_groups;
+        a.band_groups[1] = 0;
+    }
 }
 
 // Decode records for pa_decode_append_noalloc: a fixed array on each device
@@ -279,9 +303,10 @@ int decode_impl(void* out, const void* q, const void* key, const void* value, co
     a.n_kvg = num_kv_heads * a.groups_per_kv;
     // wave groups of n_kvg waves (one per head group), as many as fit the
     // persistent grid and the workspace records
-    a.wave_groups = std::max(1, std::min(decode_waves(pa::kDecodeWavesPerCU), pa::kDecodeMaxWaves) / a.n_kvg);
-    if ((long long)a.wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
-    a.waves = a.wave_groups * a.n_kvg;
+    const int wave_groups = std::max(1, std::min(decode_waves(pa::kDecodeWavesPerCU), pa::kDecodeMaxWaves) / a.n_kvg);
+    if ((long long)wave_groups * a.n_kvg > pa::kDecodeMaxWaves) return PA_EUNSUPPORTED;
+    decode_bands(a, wave_groups, num_kv_heads, dtype == PA_BF16 && !kv8 && head_dim == 128);
+    a.waves = (a.band_groups[0] + a.band_groups[1]) * a.band_heads;
     // a caller's workspace is laid out for every launch shape; the fixed
     // scratch for exactly this call's waves, and it must hold them
     const DecodeWsLayout ws = static_scratch ? decode_ws_layout(gp, head_dim, a.waves) : decode_ws_layout(gp, head_dim);

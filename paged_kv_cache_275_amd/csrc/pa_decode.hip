@@ -21,6 +21,10 @@
 //    sequence in a range adds switch_ticks for closing its segment, so waves
 //    with many short sequences get fewer blocks.  Consecutive units of a wave
 //    are consecutive blocks of one (sequence, head group) SEGMENT.
+//    With 2 KB bf16 rows (8 kv heads, head_dim 128) the head groups form two
+//    BANDS (kv heads 0-3 and 4-7), each with groups of 4 waves and its own
+//    split; the second half of a token row streams slower, so the second band
+//    gets a few more groups (DecodeArgs, decode_bands in pa_api.hip).
 //  * Each wave owns ALL query heads (up to GP) that share the kv head, so every
 //    K/V byte is read from HBM exactly once and reused from registers by the
 //    whole GQA group.
@@ -470,7 +474,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     const int C = a.switch_ticks;
     prefix_blocks<NW * kWave>(pref, tpref, lens, scan_scratch, a.context_lens, S, R, C);
     __syncthreads();
-    const int n_kvg = a.n_kvg;
     const long long TT = tpref[S];  // ticks of one head group over all sequences
     if (threadIdx.x < kWave) {
         // sequences without tokens get zero rows: wave 0 of every workgroup
@@ -486,7 +489,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             }
         }
     }
-    const long long NG = a.wave_groups;
     // wave index, made wave-uniform explicitly: everything the wave decides
     // (ranges, segment walk, branches) derives from it, and the compiler would
     // otherwise treat threadIdx-derived values as per-lane and turn the whole
@@ -500,8 +502,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
     const int wv = __builtin_amdgcn_readfirstlane(vwg * NW + threadIdx.x / kWave);
     if (wv >= a.waves) return;  // padding waves of the last workgroup (no barrier follows)
     const int lane = threadIdx.x & (kWave - 1);
-    const int kvg = wv % n_kvg;                  // this wave's head group
-    const long long grp = wv / n_kvg;            // its wave group
+    const int hb = a.band_heads;
+    const bool band1 = wv >= a.band_groups[0] * hb;
+    const int band_wave0 = band1 ? a.band_groups[0] * hb : 0;  // the band's first wave
+    const int band_kvg0 = band1 ? hb : 0;                       // the band's first head group
+    const long long NG = a.band_groups[band1 ? 1 : 0];          // wave groups of the band
+    const int kvg = band_kvg0 + (wv - band_wave0) % hb;         // this wave's head group
+    const long long grp = (wv - band_wave0) / hb;               // its wave group in the band
     const int hk = kvg / a.groups_per_kv;        // kv head
     const int gi0 = (kvg % a.groups_per_kv) * GP;  // first query head of the group within the kv head
     const int h0 = hk * a.group + gi0;           // ... among all query heads
@@ -797,7 +804,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
             // of the segment's last block
             const long long t_last = (long long)tpref[cs] + (long long)(cnb - 1) * R;
             note.seq = cs;
-            note.last_wave = (int)(((t_last + 1) * NG - 1) / TT) * n_kvg + kvg;
+            note.last_wave = band_wave0 + (int)(((t_last + 1) * NG - 1) / TT) * hb + (kvg - band_kvg0);
             note.first_slot = slot;
         }
         first_seg = false;
@@ -1022,8 +1029,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 
 // Merge the partial records of the split segment noted by wave w (if any):
 //   M = max_v m_v,  L = sum_v l_v 2^(m_v - M),  out = sum_v acc_v 2^(m_v - M) / L
-// over the waves v = w, w + n_kvg, ..., last_wave (the waves of the segment's
-// head group in consecutive wave groups) that hold its units, folded in record
+// over the waves v = w, w + band_heads, ..., last_wave (the waves of the
+// segment's head group in consecutive wave groups of its band) that hold its
+// units, folded in record
 // order with a running maximum.  One workgroup per noting wave, one wave per
 // head.  The note is one memory round trip; the (max, sum) pairs and sums of up
 // to kBatch records are then loaded together, so a merge of up to kBatch parts
@@ -1047,9 +1055,10 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
     const SplitNote sn = a.ws_split[w];
     const int gi0 = sn.seq >= 0 ? (sn.kvg % a.groups_per_kv) * GP : 0;
     const bool merging = sn.seq >= 0 && gi0 + g < a.group;
-    const int nrec = merging ? (sn.last_wave - w) / a.n_kvg + 1 : 1;  // waves w, w + n_kvg, ..., last_wave
-    auto rec_of = [&](int j) __attribute__((always_inline)) -> size_t {  // record of wave w + j * n_kvg, head g
-        return ((size_t)(w + j * a.n_kvg) * 2 + (j == 0 ? sn.first_slot : 0)) * GP + g;
+    const int hb = a.band_heads;
+    const int nrec = merging ? (sn.last_wave - w) / hb + 1 : 1;  // waves w, w + hb, ..., last_wave
+    auto rec_of = [&](int j) __attribute__((always_inline)) -> size_t {  // record of wave w + j * hb, head g
+        return ((size_t)(w + j * hb) * 2 + (j == 0 ? sn.first_slot : 0)) * GP + g;
     };
     // lane b loads the (max, sum) of record j0 + b (one vector load for the
     // batch), every lane its kPerLane sums of each record; records past nrec

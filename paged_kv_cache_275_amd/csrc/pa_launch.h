@@ -28,13 +28,16 @@ constexpr int kDecodeMaxSeqs = 8192;    // sequence prefix sums live in LDS
 // units when the units are shared out among the waves.
 constexpr int kDecodeUnitTicks = 4;
 constexpr int kDecodeSwitchTicks = 4;
+// Wave groups of the second band over the first, where the head groups are
+// split in two bands (pa_api.hip, decode_bands).
+constexpr double kDecodeBandRatio = 1.032;
 
 // A segment (sequence, head group) whose units were split across waves, noted
 // by the wave that holds its first unit.  seq < 0: no split segment starts in
 // that wave.  The segment's records are slot first_slot of the noting wave and
-// slot 0 of the waves of the same head group in the following wave groups
-// (every n_kvg-th wave) up to last_wave; waves with an empty range leave a
-// record of zero weight there.
+// slot 0 of the waves of the same head group in the following wave groups of
+// its band (every band_heads-th wave) up to last_wave; waves with an empty
+// range leave a record of zero weight there.
 struct SplitNote {
     int seq;
     int kvg;
@@ -65,8 +68,14 @@ struct DecodeArgs {
     int group;          // query heads per kv head
     int groups_per_kv;  // head groups (of up to GP heads) per kv head
     int n_kvg;          // num_kv_heads * groups_per_kv
-    int waves;          // working waves: wave_groups * n_kvg (the grid is rounded up to whole workgroups)
-    int wave_groups;    // groups of n_kvg waves; group g streams the g-th share of all blocks
+    // The head groups are split into bands of band_heads consecutive head
+    // groups (one band, band_heads = n_kvg, or two halves).  Band b has
+    // band_groups[b] wave GROUPS of band_heads waves; group g of band b
+    // streams the g-th of band_groups[b] equal shares of all blocks for the
+    // band's head groups.  Waves are numbered band by band.
+    int band_heads;
+    int band_groups[2];  // band_groups[1] = 0 with one band
+    int waves;           // working waves: (band_groups[0] + band_groups[1]) * band_heads
     int unit_ticks;     // work-split cost of one unit (one block of one head group)
     int switch_ticks;   // extra cost of closing a segment (one head group of a sequence)
     float scale_log2;   // scale * log2(e) (times k_scale for an fp8 cache)
