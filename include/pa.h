@@ -254,9 +254,9 @@ int pa_decode_append_timed(void *out, const void *q, const void *key, const void
 
 /*
  * Launch shape of every later pa_decode* call in this process (all threads):
- * waves of the persistent streaming grid (0 = 4 per compute unit, 8 for an fp8
- * cache when two workgroups fit a compute unit; at most 4096, rounded down to a
- * multiple of 4), blocks in flight per wave (0 = the default 2; else 2, 3 or 4,
+ * waves of the persistent streaming grid (0 = 4 per compute unit, for every
+ * cache type; at most 4096, rounded down to a multiple of 4), blocks in flight
+ * per wave (0 = the default 2; else 2, 3 or 4,
  * and for fp8 caches also 6 or 8) and the extra work-split cost of closing a
  * sequence in units of a quarter block (-1 = the default 4; else 0..64).  The
  * results of decode do not depend on these choices; they move only the split
