@@ -1035,7 +1035,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_stream_kernel(DecodeArgs a)
 // order with a running maximum.  One workgroup per noting wave, one wave per
 // head.  The note is one memory round trip; the (max, sum) pairs and sums of up
 // to kBatch records are then loaded together, so a merge of up to kBatch parts
-// costs two dependent round trips.  In the fused call the workgroup first
+// costs two dependent round trips.  Segments of more than kLongMin parts (a
+// long context spread over many waves) take a two-pass merge instead: the
+// (max, sum) pairs of every part at once, then the sums kLongBatch parts at a
+// time with precomputed weights.  In the fused call the workgroup first
 // copies new K/V rows into the cache (see below).  Records of zero weight (m = -inf: waves
 // whose range was empty) are skipped without touching their sums.
 //
@@ -1048,6 +1051,9 @@ template <typename T, int D, int GP>
 __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) {
     constexpr int kPerLane = D / kWave;  // 1 or 2
     constexpr int kBatch = 8;
+    constexpr int kLongMin = 16;     // segments of more parts, up to kLongChunks * 64,
+    constexpr int kLongChunks = 4;   // take the two-pass merge
+    constexpr int kLongBatch = 32;   // sums loaded together in the two-pass merge (divides kWave)
     const int nb = (int)gridDim.x;  // = a.waves
     const int w = nb % 8 == 0 ? (int)(blockIdx.x % 8) * (nb / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -1075,7 +1081,24 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
             for (int i = 0; i < kPerLane; ++i) x[b][i] = a.ws_acc[r * D + lane * kPerLane + i];
         }
     };
-    if (merging) load_batch(0);  // in flight while the copy below resolves its slot
+    // the two-pass merge (below) for segments of many parts
+    const bool long_merge = merging && nrec > kLongMin && nrec <= kLongChunks * kWave;
+    float2 mlc[kLongChunks];
+    if (long_merge) {
+        // (max, sum) of record j in lane j % 64 of chunk j / 64, all loaded together
+#pragma unroll
+        for (int c = 0; c < kLongChunks; ++c) {
+            const int j = c * kWave + lane;
+            mlc[c] = make_float2(-INFINITY, 0.f);
+            if (c * kWave < nrec) {  // uniform
+                const float2 v = *reinterpret_cast<const float2*>(a.ws_ml + rec_of(min(j, nrec - 1)) * 2);
+                if (j < nrec) mlc[c] = v;
+            }
+        }
+    } else if (merging) {
+        load_batch(0);
+    }
+    // either is in flight while the copy below resolves its slot
 
     if (a.new_k != nullptr) {
         // Fused KV append: the new token's K/V rows of sequence b (and b +
@@ -1118,7 +1141,52 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
     float M = -INFINITY, L = 0.f, o[kPerLane];
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) o[i] = 0.f;
-    for (int j0 = 0; j0 < nrec; j0 += kBatch) {
+    if (long_merge) {
+        // A segment of many parts (a long context over many waves): the
+        // (max, sum) pairs of all its records came first; their maximum and
+        // the normaliser are wave reductions, and each record's weight
+        // 2^(m - M) / L stays in its lane.  The sums are then loaded
+        // kLongBatch records at a time and added with those weights: a few
+        // round trips in all instead of one per kBatch records, and no
+        // dependency from one record to the next.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < kLongChunks; ++c) mx = fmaxf(mx, mlc[c].x);
+        M = wave_max64(mx);  // finite: the noting wave's own part holds units
+        float ls = 0.f;
+        float wgt[kLongChunks];
+#pragma unroll
+        for (int c = 0; c < kLongChunks; ++c) {
+            wgt[c] = mlc[c].x != -INFINITY ? fast_exp2(mlc[c].x - M) : 0.f;  // zero-weight records stay 0
+            ls += mlc[c].y * wgt[c];
+        }
+        L = wave_sum64(ls);
+        const float invl = 1.f / L;
+#pragma unroll
+        for (int c = 0; c < kLongChunks; ++c) wgt[c] *= invl;
+        float xs[kLongBatch][kPerLane];
+        for (int j0 = 0; j0 < nrec; j0 += kLongBatch) {
+#pragma unroll
+            for (int b = 0; b < kLongBatch; ++b) {
+                const size_t r = rec_of(min(j0 + b, nrec - 1));
+#pragma unroll
+                for (int i = 0; i < kPerLane; ++i) xs[b][i] = a.ws_acc[r * D + lane * kPerLane + i];
+            }
+            const int c = j0 / kWave;  // kLongBatch divides kWave: one chunk per batch
+            float wc = wgt[0];
+#pragma unroll
+            for (int k = 1; k < kLongChunks; ++k) wc = c == k ? wgt[k] : wc;
+#pragma unroll
+            for (int b = 0; b < kLongBatch; ++b) {
+                const float wb = readlane_f32(wc, (j0 % kWave) + b);  // 0 past the segment
+                // a zero weight skips the record's sums (never written for empty ranges)
+#pragma unroll
+                for (int i = 0; i < kPerLane; ++i) o[i] = wb != 0.f ? fmaf(xs[b][i], wb, o[i]) : o[i];
+            }
+        }
+        L = 1.f;  // the weights carried 1 / L
+    } else {
+      for (int j0 = 0; j0 < nrec; j0 += kBatch) {
         if (j0 > 0) load_batch(j0);
         float2 ml[kBatch];
 #pragma unroll
@@ -1134,6 +1202,7 @@ __global__ __launch_bounds__(GP * kWave) void decode_fixup_kernel(DecodeArgs a) 
             for (int i = 0; i < kPerLane; ++i) o[i] = o[i] * ca + (live ? x[b][i] * cb : 0.f);
             M = mn;
         }
+      }
     }
     const float inv = 1.f / L;
     T* orow = reinterpret_cast<T*>(a.out) + ((size_t)sn.seq * a.num_q_heads + hk * a.group + gi0 + g) * D +

@@ -22,6 +22,9 @@ constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
 constexpr int kDppRowRor8 = 0x128;     // lane i <- lane (i+8) mod 16 within a row
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor2 = 0x122;
+constexpr int kDppRowRor1 = 0x121;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -127,6 +130,23 @@ __device__ __forceinline__ float max_rows4(float x) {
         x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
     }
     return x;
+}
+
+// Max and sum over all 64 lanes (every lane gets the result): DPP rotations
+// within each 16-lane row, then the permlane swaps across rows.
+__device__ __forceinline__ float wave_max64(float x) {
+    x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+    x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+    x = fmaxf(x, dpp_f32<kDppRowRor2>(x));
+    x = fmaxf(x, dpp_f32<kDppRowRor1>(x));
+    return max_rows4(x);
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+    x += dpp_f32<kDppRowRor8>(x);
+    x += dpp_f32<kDppRowRor4>(x);
+    x += dpp_f32<kDppRowRor2>(x);
+    x += dpp_f32<kDppRowRor1>(x);
+    return sum_rows4(x);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
