@@ -402,6 +402,21 @@ def test_decode_and_prefill_in_a_pool_beyond_4gib():
     assert_attention_close(widen_dev(pout), pref, "bf16", "prefill, pool > 4 GiB")
 
 
+@pytest.mark.parametrize("waves", [8, 12, 16, 20, 256, 300])
+def test_decode_merge_paths(waves):
+    """One long context split over every wave of a small grid (one kv head:
+    each wave is a wave group of its own, so the context has about as many
+    parts as there are waves).  That reaches each way the merge kernel folds
+    a segment: 8 parts (one batch of records), 12 and 16 (a second batch), 20
+    and 256 (the two-pass merge for many parts), 300 (beyond the two-pass
+    limit, batched again)."""
+    rng = np.random.default_rng(900 + waves)
+    q, kc, vc, bt, lens = _random_bf16_case(rng, 4, 1, 128, [8192, 33, 1])
+    with ops.decode_launch(waves=waves):
+        got = _decode_bf16(q, kc, vc, bt, lens, 0.05)
+    assert_attention_close(got, oracle.decode(q, kc, vc, bt, lens, 0.05), "bf16", f"waves {waves}")
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(64, 1, 128), (128, 2, 64)])
 def test_decode_largest_group(hq, hkv, d):
     """64 query heads per kv head, the most a call takes (8 head groups of 8)."""
