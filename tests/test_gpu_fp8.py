@@ -71,10 +71,14 @@ def test_fp8_append_and_decode_small(name, num_seqs, seed):
     _check_fp8(wl, f"{name}/s{seed}/n{num_seqs}")
 
 
-def test_fp8_full_size_llama3_8b():
-    """The decode workload the benchmark times (128 sequences, 64..4096 tokens)."""
-    wl = W.make_workload("llama3_8b", seed=W.CONFIG_NAMES.index("llama3_8b"))
-    _check_fp8(wl, "llama3_8b/full")
+@pytest.mark.parametrize("name,seed_offset", [("llama3_8b", 0), ("llama3_8b", 100), ("llama3_8b", 200),
+                                              ("long_skewed", 0)])
+def test_fp8_full_size(name, seed_offset):
+    """Full-size decode workloads over fp8 caches: the one the benchmark times
+    (128 sequences, 64..4096 tokens) at its seed and at seeds + 100 and + 200,
+    and the skewed one (a 65536-token context beside Pareto-distributed ones)."""
+    wl = W.make_workload(name, seed=W.CONFIG_NAMES.index(name) + seed_offset)
+    _check_fp8(wl, f"{name}/full/+{seed_offset}")
 
 
 @pytest.mark.parametrize("src", ["f32", "bf16"])
